@@ -1,0 +1,221 @@
+"""Throughput of the block-sparse attention path on one MI355X.
+
+A step is one pass of the selection + attention path over the 64K-token
+workload (batch 1, 32 heads, 65536 tokens, head_dim 128, block 128, top-128
+of 512 key blocks per query block, bf16): pool Q, pool K, block scores +
+top-k, block-sparse attention emitting O (bf16) and LSE (float32).  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+The headline value is kept-block attention TFLOP/s of the whole step
+(4 * 128^3 flops per kept (query block, key block) pair, nothing else
+counted).  Also reported: per-kernel times from HIP events on the launch
+stream, the roofline of the attention kernel, the two-way LSE merge on
+64K-shaped partials, and the fp64 CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="dlm64k", choices=["dlm64k", "dlm16k"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-stages", action="store_true", help="skip the merge stage measurement")
+    return p.parse_args()
+
+
+def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    pooling + scoring + top-k of one head, then whole query tiles of that head's
+    attention until the time budget is used.  Extrapolated linearly to the whole
+    step and expressed in the same unit as the GPU value."""
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    h = 0
+    t0 = time.perf_counter()
+    qb = orc.pool_mean(x["q"][:, h:h + 1], w.block)
+    kb = orc.pool_mean(x["k"][:, h:h + 1], w.block)
+    idx = orc.topk_ascending(orc.block_logits(qb, kb, w.scale), w.topk)
+    t_sel_head = time.perf_counter() - t0
+    kh, vh = orc.as_f64(x["k"][0, h]), orc.as_f64(x["v"][0, h])
+    tiles = 0
+    t1 = time.perf_counter()
+    while tiles < 2 or (time.perf_counter() - t1 < budget_s and tiles < w.blocks):
+        rows = x["q"][0, h, tiles * w.block:(tiles + 1) * w.block]
+        orc.attend_rows(rows, kh, vh, idx[0, 0, tiles], w.block, w.scale)
+        tiles += 1
+    t_tile = (time.perf_counter() - t1) / tiles
+    est = t_sel_head * w.heads + t_tile * w.heads * w.blocks
+    flops = 4.0 * w.block ** 3 * w.heads * w.blocks * w.topk
+    return {"value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0: pool+score+top-k ({t_sel_head:.2f} s) and {tiles} of {w.blocks} "
+                      f"query tiles of attention ({t_tile:.3f} s each); scaled linearly to "
+                      f"{w.heads} heads (est. {est:.0f} s for the whole step)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "(batch, head) with no exchange, so N GPUs run N independent copies.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import block_sparse_attention_mean_amd as basa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = wl.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = wl.generate(w.name)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    nb = w.blocks
+    shp = (1, w.heads)
+    qbar = torch.empty(*shp, nb, w.head_dim, dtype=torch.float64, device="cuda")
+    kbt = torch.empty(*shp, w.head_dim, nb, dtype=torch.float64, device="cuda")
+    idx = torch.empty(*shp, nb, w.topk, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(*shp, w.tokens, dtype=torch.float32, device="cuda")
+    seg = basa.kv_segment(idx, k, v)
+
+    ev = {name: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+          for name in ("pool", "select", "attn")}
+
+    def step(i=None):
+        if i is not None:
+            ev["pool"][2 * i].record()
+        basa.basa_pool(q, w.block, mean_rows=qbar)
+        basa.basa_pool(k, w.block, mean_cols=kbt)
+        if i is not None:
+            ev["pool"][2 * i + 1].record()
+            ev["select"][2 * i].record()
+        basa.basa_select(qbar, kbt, idx, w.topk, scale=w.scale)
+        if i is not None:
+            ev["select"][2 * i + 1].record()
+            ev["attn"][2 * i].record()
+        basa.basa_attn(q, seg, o, lse, tile_q=w.block, block_k=w.block, scale=w.scale)
+        if i is not None:
+            ev["attn"][2 * i + 1].record()
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def avg_ms(name):
+        e = ev[name]
+        return sum(e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(args.steps)) / args.steps
+
+    t_pool, t_sel, t_attn = avg_ms("pool"), avg_ms("select"), avg_ms("attn")
+    kept_pairs = w.heads * nb * w.topk
+    flops = 4.0 * w.block ** 3 * kept_pairs
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (t_attn * 1e-3) / 1e12
+    pool_bytes = 2 * (w.heads * w.tokens * w.head_dim * 2) + 2 * (w.heads * nb * w.head_dim * 8)
+    sel_bytes = 2 * (w.heads * nb * w.head_dim * 8) + w.heads * nb * w.topk * 4
+
+    stages = {
+        "pool_q_k": {"ms": t_pool, "GB/s": pool_bytes / (t_pool * 1e-3) / 1e9,
+                     "frac_hbm": pool_bytes / (t_pool * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "select": {"ms": t_sel, "GB/s": sel_bytes / (t_sel * 1e-3) / 1e9,
+                   "fp64_GFLOP/s": 2.0 * w.heads * nb * nb * w.head_dim / (t_sel * 1e-3) / 1e9},
+        "pool+select": {"ms": t_pool + t_sel,
+                        "frac_hbm": (pool_bytes + w.heads * nb * w.topk * 4) / ((t_pool + t_sel) * 1e-3)
+                        / 1e9 / PEAK_HBM_GBS},
+        "attn": {"ms": t_attn, "TFLOP/s": attn_tflops},
+    }
+
+    if not args.no_stages:
+        # two-way LSE merge on 64K-shaped partials: each row's kept list split in
+        # two halves, each half's attention written as float32 O + LSE, merged to bf16
+        half = w.topk // 2
+        oa = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        ob = torch.empty_like(oa)
+        la = torch.empty_like(lse)
+        lb = torch.empty_like(lse)
+        sa = basa.kv_segment(idx, k, v, count=half, offset=0)
+        sb = basa.kv_segment(idx, k, v, count=w.topk - half, offset=half)
+        basa.basa_attn(q, sa, oa, la, tile_q=w.block, block_k=w.block, scale=w.scale)
+        basa.basa_attn(q, sb, ob, lb, tile_q=w.block, block_k=w.block, scale=w.scale)
+        om = torch.empty_like(o)
+        lm = torch.empty_like(lse)
+        reps = 10
+        basa.basa_merge(oa, la, ob, lb, om, lm)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            basa.basa_merge(oa, la, ob, lb, om, lm)
+        e1.record()
+        torch.cuda.synchronize()
+        t_merge = e0.elapsed_time(e1) / reps
+        merge_bytes = 2 * (oa.numel() * 4 + la.numel() * 4) + om.numel() * 2 + lm.numel() * 4
+        stages["merge"] = {"ms": t_merge, "GB/s": merge_bytes / (t_merge * 1e-3) / 1e9,
+                           "frac_hbm": merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "max_abs_vs_one_shot": float((om.float() - o.float()).abs().max())}
+        del oa, ob, la, lb, om, lm
+
+    result = {
+        "metric": "block-sparse attn TFLOP/s (kept blocks) + % MFMA peak at L=64K, d=128",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch 1, {w.heads} heads, L={w.tokens}, d={w.head_dim}, "
+                               f"block {w.block}, top-{w.topk} of {nb} key blocks, bidirectional",
+                   "global_batch": 1, "seq_len": w.tokens, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "pct_mfma_peak_step": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

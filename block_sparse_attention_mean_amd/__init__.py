@@ -1,0 +1,227 @@
+"""Python binding of libbasa: argument marshalling only.
+
+Each function takes torch tensors that live on the current GPU, checks their
+dtype and layout, and calls the C function of the same name on torch's current
+stream.  Every step of the computation runs in the HIP kernels of libbasa.so;
+there is no other code path.  Importing this package fails loudly if the
+library has not been built (``python block_sparse_attention_mean_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbasa.so")
+
+F32, BF16, F64 = 0, 1, 2
+SELECT_BLOCKS, SELECT_CHANGE = 0, 1
+
+STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE",
+          4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
+
+EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_attn",
+           "basa_merge")
+
+
+class BasaError(RuntimeError):
+    def __init__(self, func: str, status: int, msg: str):
+        super().__init__(f"{func} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class SelectDesc(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("batch", ctypes.c_int64), ("heads_q", ctypes.c_int64), ("heads_kv", ctypes.c_int64),
+        ("q_len", ctypes.c_int64), ("rows", ctypes.c_int64), ("keys", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64), ("scale", ctypes.c_double),
+        ("q_rows", ctypes.c_void_p), ("parent", ctypes.c_void_p),
+        ("parent_k", ctypes.c_int32), ("fanout", ctypes.c_int32),
+    ]
+
+
+MAX_SEGMENTS = 4
+
+
+class KvSegment(ctypes.Structure):
+    _fields_ = [
+        ("idx", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("len", ctypes.c_int64), ("rows", ctypes.c_int64), ("count", ctypes.c_int32),
+        ("stride", ctypes.c_int32), ("shift", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("bias", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads_q", ctypes.c_int64), ("heads_kv", ctypes.c_int64),
+        ("len_q", ctypes.c_int64), ("head_dim", ctypes.c_int64), ("lists", ctypes.c_int64),
+        ("tile_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("seg", KvSegment * MAX_SEGMENTS),
+        ("q_rows", ctypes.c_void_p), ("scale", ctypes.c_double),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python block_sparse_attention_mean_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.basa_status_string.restype = ctypes.c_char_p
+    lib.basa_status_string.argtypes = [i32]
+    lib.basa_version.restype = i32
+    lib.basa_version.argtypes = []
+    lib.basa_pool.restype = i32
+    lib.basa_pool.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i32, vp]
+    lib.basa_select.restype = i32
+    lib.basa_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
+    lib.basa_attn.restype = i32
+    lib.basa_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, i32, vp, vp]
+    lib.basa_merge.restype = i32
+    lib.basa_merge.argtypes = [i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp]
+    return lib
+
+
+lib = _load()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise BasaError(func, status, lib.basa_status_string(status).decode())
+
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def basa_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None,
+              mean_cols: torch.Tensor | None = None, mean_copy: torch.Tensor | None = None) -> None:
+    """Block means of x [..., len, head_dim] into the given float64/float32/bf16 outputs."""
+    *lead, length, d = x.shape
+    outer = 1
+    for s in lead:
+        outer *= s
+    copy_dt = _dt(mean_copy) if mean_copy is not None else F32
+    _check("basa_pool", lib.basa_pool(_ptr(x), _dt(x), outer, length, d, block, _ptr(mean_rows),
+                                      _ptr(mean_cols), _ptr(mean_copy), copy_dt, _stream()))
+
+
+def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
+                mode: int = SELECT_BLOCKS, scale: float = 1.0, heads_kv: int | None = None,
+                keys: int | None = None, q_rows: torch.Tensor | None = None,
+                parent: torch.Tensor | None = None, fanout: int = 1) -> None:
+    """BLOCKS: q [B,Hq,Lq,d] float64 means, k [B,Hkv,d,keys] float64 transposed means,
+    idx [B,Hq,rows,topk] int32.  CHANGE: q, k [B,H,T,d] current/previous queries,
+    idx [B,topk] int32."""
+    b, hq, lq, d = q.shape
+    desc = SelectDesc()
+    desc.mode = mode
+    desc.topk = topk
+    desc.batch, desc.heads_q, desc.q_len, desc.head_dim = b, hq, lq, d
+    if mode == SELECT_CHANGE:
+        desc.heads_kv, desc.rows, desc.keys, desc.scale = hq, lq, lq, 1.0
+    else:
+        desc.heads_kv = k.shape[1] if heads_kv is None else heads_kv
+        desc.keys = k.shape[-1] if keys is None else keys
+        desc.rows = idx.shape[2]
+        desc.scale = scale
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    desc.q_rows = _ptr(q_rows)
+    desc.parent = _ptr(parent)
+    desc.parent_k = parent.shape[-1] if parent is not None else 0
+    desc.fanout = fanout
+    _check("basa_select", lib.basa_select(ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q),
+                                          _ptr(idx), _stream()))
+
+
+def kv_segment(idx: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, count: int | None = None,
+               offset: int = 0, shift: int = 0, bias: float = 0.0) -> dict:
+    """One key source for basa_attn.  idx [B,Hq,rows,stride] int32 block indices
+    (entries offset .. offset+count-1 of each row are used); k/v [B,Hkv,len,d]."""
+    if idx.dtype != torch.int32:
+        raise TypeError("segment index must be int32")
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise TypeError("segment k and v must match")
+    stride = idx.shape[-1]
+    count = stride - offset if count is None else count
+    if not 0 <= offset <= stride - count:
+        raise ValueError("segment column range out of bounds")
+    return {"idx": idx, "k": k, "v": v, "count": count, "offset": offset, "stride": stride,
+            "shift": shift, "bias": bias}
+
+
+def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, tile_q: int,
+              block_k: int, scale: float, q_rows: torch.Tensor | None = None) -> None:
+    """q [B,Hq,Lq,d]; segments from kv_segment(); o [B,Hq,Lq,d]; lse [B,Hq,Lq] float32.
+    q_rows [B, lists*tile_q] int32 selects the query rows of each tile."""
+    b, hq, lq, d = q.shape
+    if isinstance(segments, dict):
+        segments = [segments]
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError("1 to 4 segments")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    desc = AttnDesc()
+    desc.batch, desc.heads_q, desc.len_q, desc.head_dim = b, hq, lq, d
+    desc.heads_kv = segments[0]["k"].shape[1]
+    desc.lists = (q_rows.shape[-1] if q_rows is not None else lq) // tile_q
+    desc.tile_q, desc.block_k, desc.n_segments = tile_q, block_k, len(segments)
+    keep = []
+    for i, sg in enumerate(segments):
+        if sg["k"].shape[1] != desc.heads_kv:
+            raise ValueError("all segments need the same number of key heads")
+        t = desc.seg[i]
+        t.idx = _ptr(sg["idx"]) + 4 * sg["offset"]
+        t.k, t.v = _ptr(sg["k"]), _ptr(sg["v"])
+        t.len, t.rows = sg["k"].shape[2], sg["idx"].shape[2]
+        t.count, t.stride, t.shift = sg["count"], sg["stride"], sg["shift"]
+        t.dtype, t.bias = _dt(sg["k"]), sg["bias"]
+        keep.append(sg)
+    desc.q_rows = _ptr(q_rows)
+    desc.scale = scale
+    _check("basa_attn", lib.basa_attn(ctypes.byref(desc), _ptr(q), _dt(q), _ptr(o), _dt(o),
+                                      _ptr(lse), _stream()))
+
+
+def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+               o: torch.Tensor, lse: torch.Tensor) -> None:
+    """Merge two partials [..., d] + [...] into o, lse (o may be o_a)."""
+    d = o_a.shape[-1]
+    rows = o_a.numel() // d
+    if o_a.dtype != o_b.dtype:
+        raise TypeError("partials must share a dtype")
+    for t in (lse_a, lse_b, lse):
+        if t.dtype != torch.float32:
+            raise TypeError("LSE tensors must be float32")
+    _check("basa_merge", lib.basa_merge(rows, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
+                                        _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
+
+
+__all__ = ["basa_pool", "basa_select", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
+           "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
+           "SELECT_CHANGE"]

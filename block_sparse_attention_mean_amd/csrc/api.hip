@@ -1,0 +1,159 @@
+// C ABI of libbasa: host-side argument checks, then dispatch to the kernels.
+// Every check runs before any HIP call, so an invalid request enqueues nothing
+// and touches no device state.
+#include <cmath>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2_dim(int64_t d, int64_t lo, int64_t hi) {
+  return d >= lo && d <= hi && (d & (d - 1)) == 0;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? BASA_OK : BASA_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* basa_status_string(int status) {
+  switch (status) {
+    case BASA_OK: return "ok";
+    case BASA_E_NULLPTR: return "required pointer is NULL";
+    case BASA_E_SHAPE: return "inconsistent or out-of-range sizes";
+    case BASA_E_DTYPE: return "unsupported element type";
+    case BASA_E_ALIGN: return "pointer not 16-byte aligned";
+    case BASA_E_UNSUPPORTED: return "request not implemented by the kernels";
+    case BASA_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int basa_version(void) { return kVersion; }
+
+int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+              int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
+              int copy_dtype, void* stream) {
+  try {
+    if (outer < 0 || len < 0 || block < 1 || head_dim < 8 || head_dim > 512 || head_dim % 8 != 0)
+      return BASA_E_SHAPE;
+    if (len % block != 0) return BASA_E_SHAPE;
+    if (x_dtype != BASA_F32 && x_dtype != BASA_BF16 && x_dtype != BASA_F64) return BASA_E_DTYPE;
+    if (mean_copy && copy_dtype != BASA_F32 && copy_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (outer * len == 0) return BASA_OK;
+    if (!x || (!mean_rows && !mean_cols && !mean_copy)) return BASA_E_NULLPTR;
+    if (!aligned16(x) || !aligned16(mean_rows) || !aligned16(mean_cols) || !aligned16(mean_copy))
+      return BASA_E_ALIGN;
+    return from_hip(basa::launch_pool(x, x_dtype, outer, len, head_dim, block, mean_rows,
+                                      mean_cols, mean_copy, copy_dtype,
+                                      static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_select(const basa_select_desc* d, const void* q, const void* k, int dtype, int32_t* idx,
+                void* stream) {
+  try {
+    if (!d) return BASA_E_NULLPTR;
+    if (d->batch < 0 || d->heads_q < 1 || d->q_len < 0 || d->topk < 1) return BASA_E_SHAPE;
+    if (d->head_dim < 8 || d->head_dim > 512 || d->head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (d->mode == BASA_SELECT_CHANGE) {
+      if (dtype != BASA_F32 && dtype != BASA_BF16 && dtype != BASA_F64) return BASA_E_DTYPE;
+      if (d->q_len > 1024 || d->topk > d->q_len) return BASA_E_SHAPE;
+      if (d->batch == 0) return BASA_OK;
+      if (!q || !k || !idx) return BASA_E_NULLPTR;
+      if (!aligned16(q) || !aligned16(k)) return BASA_E_ALIGN;
+      return from_hip(basa::launch_select_change(d, q, k, dtype, idx,
+                                                 static_cast<hipStream_t>(stream)));
+    }
+    if (d->mode != BASA_SELECT_BLOCKS) return BASA_E_UNSUPPORTED;
+    if (dtype != BASA_F64) return BASA_E_DTYPE;
+    if (d->heads_kv < 1 || d->heads_q % d->heads_kv != 0) return BASA_E_SHAPE;
+    if (d->rows < 0 || d->keys < 1 || d->keys > 4096) return BASA_E_SHAPE;
+    if (!(d->scale > 0.0) || !std::isfinite(d->scale)) return BASA_E_SHAPE;
+    if (!d->q_rows && d->rows != d->q_len) return BASA_E_SHAPE;
+    int64_t n_cand = d->keys;
+    if (d->parent) {
+      if (d->q_rows) return BASA_E_UNSUPPORTED;
+      if (d->parent_k < 1 || d->fanout < 1) return BASA_E_SHAPE;
+      n_cand = (int64_t)d->parent_k * d->fanout;
+      if (n_cand > 4096 || d->rows % d->fanout != 0 || d->keys % d->fanout != 0)
+        return BASA_E_SHAPE;
+    }
+    if (d->topk > n_cand) return BASA_E_SHAPE;
+    if (d->batch == 0 || d->rows == 0) return BASA_OK;
+    if (!q || !k || !idx) return BASA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(k)) return BASA_E_ALIGN;
+    return from_hip(basa::launch_select_blocks(d, static_cast<const double*>(q),
+                                               static_cast<const double*>(k), idx,
+                                               static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int o_dtype,
+              float* lse, void* stream) {
+  try {
+    if (!d) return BASA_E_NULLPTR;
+    if (q_dtype != BASA_F32 && q_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (o_dtype != BASA_F32 && o_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (d->batch < 0 || d->heads_q < 1 || d->heads_kv < 1 || d->heads_q % d->heads_kv != 0)
+      return BASA_E_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return BASA_E_SHAPE;
+    if (d->len_q < 0 || d->lists < 0) return BASA_E_SHAPE;
+    if (d->tile_q < 1 || d->tile_q > 128 || d->block_k < 1 || d->block_k > 4096) return BASA_E_SHAPE;
+    if (d->n_segments < 1 || d->n_segments > BASA_MAX_SEGMENTS) return BASA_E_SHAPE;
+    if (!std::isfinite(d->scale)) return BASA_E_SHAPE;
+    if (!d->q_rows && d->lists * d->tile_q != d->len_q) return BASA_E_SHAPE;
+    for (int i = 0; i < d->n_segments; ++i) {
+      const basa_kv_segment& g = d->seg[i];
+      if (g.dtype != BASA_F32 && g.dtype != BASA_BF16) return BASA_E_DTYPE;
+      if (g.count < 0 || g.count > 65536 || g.stride < g.count || g.len < 0) return BASA_E_SHAPE;
+      if (g.shift < 0 || g.shift > 30 || !std::isfinite(g.bias)) return BASA_E_SHAPE;
+      if (d->lists > 0 && g.count > 0 && g.rows < ((d->lists - 1) >> g.shift) + 1) return BASA_E_SHAPE;
+    }
+    if (d->batch == 0 || d->lists == 0) return BASA_OK;
+    if (!q || !o || !lse) return BASA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(o)) return BASA_E_ALIGN;
+    for (int i = 0; i < d->n_segments; ++i) {
+      const basa_kv_segment& g = d->seg[i];
+      if (g.count == 0) continue;
+      if (!g.idx || !g.k || !g.v) return BASA_E_NULLPTR;
+      if (!aligned16(g.k) || !aligned16(g.v)) return BASA_E_ALIGN;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (basa::attn_mfma_supported(d, q_dtype, o_dtype))
+      return from_hip(basa::launch_attn_mfma(d, q, o, o_dtype, lse, s));
+    return from_hip(basa::launch_attn_generic(d, q, q_dtype, o, o_dtype, lse, s));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse_a,
+               const void* o_b, const float* lse_b, int in_dtype, void* o, int o_dtype,
+               float* lse, void* stream) {
+  try {
+    if (rows < 0 || !is_pow2_dim(head_dim, 8, 512)) return BASA_E_SHAPE;
+    if (in_dtype != BASA_F32 && in_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (o_dtype != BASA_F32 && o_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (rows == 0) return BASA_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return BASA_E_NULLPTR;
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return BASA_E_ALIGN;
+    if (o == o_a && o_dtype != in_dtype) return BASA_E_UNSUPPORTED;
+    if (o == o_b && o_dtype != in_dtype) return BASA_E_UNSUPPORTED;
+    return from_hip(basa::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, in_dtype, o,
+                                       o_dtype, lse, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+// Block selection: block scores and a per-row top-k (BA-Att section 3.1, Eq. 2
+// and Algorithm 1), optionally restricted to the children of a parent's picks
+// (log-linear README, coarse-to-fine descent); and the LoSA active-token pick
+// by query change.
+//
+// BLOCKS mode.  One wavefront owns RW query rows of one head; lane l owns the
+// candidates l, l+64, l+128, ... so a row's scores sit in registers, KPL per
+// lane.  Scores are float64 dot products.  Keys are read from the transposed
+// means [head_dim][keys], so at each channel the lanes read consecutive keys
+// (one coalesced load per 64 candidates); the query values are wave-uniform
+// and come through the scalar cache.  The four waves of a workgroup work on
+// neighbouring rows of the same head and share the key loads in L1.
+//
+// Top-k per row, in registers: scores become order-preserving 64-bit keys; a
+// bitwise search from the top bit finds the largest threshold T with at least
+// k keys >= T (ballot + popcount per step), stopping as soon as exactly k keys
+// clear it.  If it never does, T is the k-th largest key, and the keys equal to
+// T are taken in candidate order until k are kept (ties to the lower index).
+// The kept candidates are written in candidate order, which is ascending key
+// order, with ballot prefix counts.
+#include "common.h"
+
+namespace basa {
+namespace {
+
+struct SelArgs {
+  const double* q;      // [B][Hq][q_len][d]
+  const double* kt;     // [B][Hkv][d][keys]
+  int32_t* idx;         // [B][Hq][rows][topk]
+  const int32_t* q_rows;
+  const int32_t* parent;
+  int64_t q_len, rows, keys;
+  int d, topk, group, heads_q, heads_kv, parent_k, fanout, n_cand;
+};
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+template <int KPL, int RW>
+__global__ __launch_bounds__(256) void select_blocks_kernel(SelArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
+  if (row0 >= a.rows) return;
+  const int hk = h / a.group;
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+
+  // candidate key index per lane slot (-1 = no candidate)
+  int cand[KPL];
+  if (a.parent) {
+    const int32_t* par = a.parent + (((int64_t)b * a.heads_q + h) * (a.rows / a.fanout) + row0 / a.fanout) * a.parent_k;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = lane + 64 * j;
+      cand[j] = -1;
+      if (c < a.n_cand) {
+        const int32_t pv = par[c / a.fanout];
+        const int64_t key = (int64_t)pv * a.fanout + (c % a.fanout);
+        if (pv >= 0 && key < a.keys) cand[j] = (int)key;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = lane + 64 * j;
+      cand[j] = c < a.n_cand ? c : -1;
+    }
+  }
+
+  // query row pointers (wave-uniform)
+  const double* qp[RW];
+  bool rvalid[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int64_t r = row0 + i;
+    rvalid[i] = r < a.rows;
+    int64_t qr = rvalid[i] ? r : row0;
+    if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + qr];
+    if (qr < 0 || qr >= a.q_len) qr = 0;  // a row map entry outside q reads row 0
+    qr = __builtin_amdgcn_readfirstlane((int)qr);
+    qp[i] = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
+  }
+
+  double acc[RW][KPL];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
+
+  for (int c = 0; c < a.d; ++c) {
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kv[j] = cand[j] >= 0 ? kt[(int64_t)c * a.keys + cand[j]] : 0.0;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const double qv = qp[i][c];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
+    }
+  }
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if (!rvalid[i]) continue;
+    // order-preserving keys, kept in the score registers
+    uint64_t* key = reinterpret_cast<uint64_t*>(acc[i]);
+    int n_valid = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      key[j] = cand[j] >= 0 ? ordered_key(acc[i][j]) : 0ull;
+      n_valid += popc64(__ballot(cand[j] >= 0));
+    }
+    const int k = a.topk;
+    uint64_t thr = 0;
+    bool exact = false;
+    if (n_valid == k) {
+      exact = true;  // every candidate is kept; keys of valid candidates are > 0
+      thr = 1;
+    } else {
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t t = thr | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) cnt += popc64(__ballot(cand[j] >= 0 && key[j] >= t));
+        if (cnt >= k) {
+          thr = t;
+          if (cnt == k) { exact = true; break; }
+        }
+      }
+    }
+    int need_eq = 0;
+    if (!exact) {
+      int gt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) gt += popc64(__ballot(cand[j] >= 0 && key[j] > thr));
+      need_eq = k - gt;
+    }
+    int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row0 + i) * k;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      bool sel;
+      if (exact) {
+        sel = cand[j] >= 0 && key[j] >= thr;
+      } else {
+        const bool eq = cand[j] >= 0 && key[j] == thr;
+        const uint64_t em = __ballot(eq);
+        const int eq_rank = eq_seen + popc64(em & below);
+        eq_seen += popc64(em);
+        sel = (cand[j] >= 0 && key[j] > thr) || (eq && eq_rank < need_eq);
+      }
+      const uint64_t m = __ballot(sel);
+      if (sel) out[base + popc64(m & below)] = cand[j];
+      base += popc64(m);
+    }
+  }
+}
+
+template <int KPL, int RW>
+hipError_t launch_kr(const SelArgs& a, int64_t batch, hipStream_t s) {
+  const int64_t rows_per_wg = 4 * RW;
+  dim3 grid((unsigned)((a.rows + rows_per_wg - 1) / rows_per_wg), (unsigned)a.heads_q, (unsigned)batch);
+  select_blocks_kernel<KPL, RW><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// CHANGE mode: per token, mean over heads and channels of (cur - prev)^2 in
+// float64; the topk largest (ties to the lower token), ascending.  One
+// workgroup per batch entry; wave w sums tokens w, w+4, ...
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void select_change_kernel(const T* __restrict__ cur,
+                                                            const T* __restrict__ prev, int heads,
+                                                            int tokens, int d, int topk,
+                                                            int32_t* __restrict__ idx) {
+  __shared__ double mse[1024];
+  __shared__ int keep[1024];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < tokens; t += 4) {
+    double s = 0.0;
+    for (int h = 0; h < heads; ++h) {
+      const int64_t base = (((int64_t)b * heads + h) * tokens + t) * d;
+      for (int c = lane; c < d; c += 64) {
+        double x, y;
+        if constexpr (sizeof(T) == 2) {
+          x = (double)bf16_bits_to_f32(cur[base + c]);
+          y = (double)bf16_bits_to_f32(prev[base + c]);
+        } else {
+          x = (double)cur[base + c];
+          y = (double)prev[base + c];
+        }
+        const double df = x - y;
+        s = __builtin_fma(df, df, s);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) mse[t] = s / ((double)heads * (double)d);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < tokens; t += 256) {
+    const double v = mse[t];
+    int rank = 0;
+    for (int u = 0; u < tokens; ++u) {
+      const double w = mse[u];
+      rank += (w > v || (w == v && u < t)) ? 1 : 0;
+    }
+    keep[t] = rank < topk ? 1 : 0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < tokens; t += 256) {
+    if (!keep[t]) continue;
+    int pos = 0;
+    for (int u = 0; u < t; ++u) pos += keep[u];
+    idx[(int64_t)b * topk + pos] = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, const double* kt,
+                                int32_t* idx, hipStream_t s) {
+  SelArgs a;
+  a.q = q;
+  a.kt = kt;
+  a.idx = idx;
+  a.q_rows = d->q_rows;
+  a.parent = d->parent;
+  a.q_len = d->q_len;
+  a.rows = d->rows;
+  a.keys = d->keys;
+  a.d = (int)d->head_dim;
+  a.topk = d->topk;
+  a.heads_q = (int)d->heads_q;
+  a.heads_kv = (int)d->heads_kv;
+  a.group = (int)(d->heads_q / d->heads_kv);
+  a.parent_k = d->parent ? d->parent_k : 0;
+  a.fanout = d->parent ? d->fanout : 1;
+  a.n_cand = d->parent ? d->parent_k * d->fanout : (int)d->keys;
+  if (a.rows == 0 || d->batch == 0 || d->heads_q == 0) return hipSuccess;
+  // rows per wave: share each key load across rows while RW*KPL stays <= 32
+  // doubles; with a parent list all rows of a wave must share one parent
+  const int kpl = (a.n_cand + 63) / 64;
+  const bool one_row = d->parent && (a.fanout % 4) != 0;
+  if (kpl <= 1) return one_row ? launch_kr<1, 1>(a, d->batch, s) : launch_kr<1, 4>(a, d->batch, s);
+  if (kpl <= 2) return one_row ? launch_kr<2, 1>(a, d->batch, s) : launch_kr<2, 4>(a, d->batch, s);
+  if (kpl <= 4) return one_row ? launch_kr<4, 1>(a, d->batch, s) : launch_kr<4, 4>(a, d->batch, s);
+  if (kpl <= 8) return one_row ? launch_kr<8, 1>(a, d->batch, s) : launch_kr<8, 4>(a, d->batch, s);
+  if (kpl <= 16) return launch_kr<16, 1>(a, d->batch, s);
+  if (kpl <= 32) return launch_kr<32, 1>(a, d->batch, s);
+  return launch_kr<64, 1>(a, d->batch, s);
+}
+
+hipError_t launch_select_change(const basa_select_desc* d, const void* q, const void* k, int dtype,
+                                int32_t* idx, hipStream_t s) {
+  if (d->batch == 0) return hipSuccess;
+  dim3 grid((unsigned)d->batch);
+  const int H = (int)d->heads_q, T = (int)d->q_len, D = (int)d->head_dim;
+  if (dtype == BASA_BF16)
+    select_change_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(q),
+                                                        static_cast<const uint16_t*>(k), H, T, D,
+                                                        d->topk, idx);
+  else if (dtype == BASA_F32)
+    select_change_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(q),
+                                                     static_cast<const float*>(k), H, T, D,
+                                                     d->topk, idx);
+  else
+    select_change_kernel<double><<<grid, 256, 0, s>>>(static_cast<const double*>(q),
+                                                      static_cast<const double*>(k), H, T, D,
+                                                      d->topk, idx);
+  return hipGetLastError();
+}
+
+}  // namespace basa

@@ -1,0 +1,233 @@
+/*
+ * basa.h - block-sparse bidirectional attention with mean-pooled block
+ * selection, for AMD Instinct MI355X (gfx950).
+ *
+ * The library exposes the four steps of the path as plain C calls:
+ *
+ *   basa_pool    mean of each run of `block` consecutive rows
+ *   basa_select  block scores (pooled Q times pooled K transposed) and a
+ *                per-row top-k, or the top-k tokens by query change
+ *   basa_attn    flash-style attention with an online softmax over the key
+ *                blocks listed for each query tile; emits O and the LSE
+ *   basa_merge   combines two partial (O, LSE) results of one row
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer named as device memory must be device memory of the
+ *   current HIP device, 16-byte aligned, and stay valid until the work on
+ *   `stream` has finished.  The caller owns every buffer; the library never
+ *   allocates, frees or keeps device memory.
+ * - Tensors are dense and row-major in the order their shapes are written.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work and returns; nothing synchronises the host.
+ * - Arguments are checked on the host before anything is enqueued; a
+ *   non-zero basa_status means nothing was launched.  BASA_E_LAUNCH reports a
+ *   failed kernel launch (hipGetLastError after the launch).
+ * - Inputs are never written.  Results are deterministic run to run (no
+ *   floating-point atomics).
+ * - No C++ exception crosses this interface.
+ */
+#ifndef BASA_H
+#define BASA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum basa_status {
+  BASA_OK = 0,
+  BASA_E_NULLPTR = 1,     /* a required pointer is NULL */
+  BASA_E_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  BASA_E_DTYPE = 3,       /* unsupported element type for this argument */
+  BASA_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  BASA_E_UNSUPPORTED = 5, /* valid request the kernels do not implement */
+  BASA_E_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+} basa_status;
+
+typedef enum basa_dtype {
+  BASA_F32 = 0,  /* IEEE binary32 */
+  BASA_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+  BASA_F64 = 2   /* IEEE binary64 */
+} basa_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* basa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int basa_version(void);
+
+/*
+ * basa_pool - block mean pooling.
+ *
+ * Follows the BA-Att paper (section 3.1 and Algorithm 1, "block statistics"):
+ * the representative of a block is the mean of its rows.  The log-linear
+ * README pools the same way, repeatedly, one level from the previous one.
+ *
+ *   x         device, [outer][len][head_dim] of x_dtype (F32, BF16 or F64)
+ *   mean_rows device or NULL, [outer][len/block][head_dim] float64
+ *   mean_cols device or NULL, [outer][head_dim][len/block] float64
+ *             (the same means, transposed; basa_select reads keys this way)
+ *   mean_copy device or NULL, [outer][len/block][head_dim] of copy_dtype
+ *             (F32 or BF16), the float64 mean rounded to nearest even
+ *
+ * Sums are accumulated in float64.  At least one output must be non-NULL.
+ * Errors: BASA_E_SHAPE if outer < 0, len < 0, block < 1, len % block != 0,
+ * head_dim not a multiple of 8 or above 512.  outer*len == 0 enqueues nothing.
+ */
+int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+              int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
+              int copy_dtype, void* stream);
+
+/* Selection modes of basa_select. */
+enum {
+  BASA_SELECT_BLOCKS = 0, /* top-k key rows per query row by q . k */
+  BASA_SELECT_CHANGE = 1  /* top-k tokens by mean squared query change */
+};
+
+typedef struct basa_select_desc {
+  int32_t mode;      /* BASA_SELECT_BLOCKS or BASA_SELECT_CHANGE */
+  int32_t topk;      /* entries kept per output row, >= 1 */
+  int64_t batch;
+  int64_t heads_q;   /* query heads */
+  int64_t heads_kv;  /* key heads; query head h reads key head h / (heads_q/heads_kv) */
+  int64_t q_len;     /* rows per query head in q */
+  int64_t rows;      /* output rows per query head (== q_len unless q_rows is set) */
+  int64_t keys;      /* key rows per key head */
+  int64_t head_dim;
+  double scale;      /* positive factor applied to the scores; the ranking does not depend on it */
+  /* optional row map: output row r of batch b reads query row q_rows[b*rows + r] */
+  const int32_t* q_rows;
+  /* optional candidate restriction (coarse-to-fine descent): output row r may
+     only pick among keys fanout*s + u, s in parent[b][h][r / fanout][0..parent_k),
+     u in [0, fanout).  parent rows must be ascending and lie in [0, keys/fanout). */
+  const int32_t* parent;
+  int32_t parent_k;
+  int32_t fanout;
+} basa_select_desc;
+/* (parent entries outside [0, keys/fanout) are treated as no candidate.) */
+
+/*
+ * basa_select - which keys each query row keeps.
+ *
+ * BASA_SELECT_BLOCKS follows BA-Att section 3.1, Eq. 2 and Algorithm 1: the
+ * block logit is the scaled dot product of the pooled query and pooled key,
+ * the block distribution is its softmax over key blocks, and each query block
+ * keeps the top-k key blocks.  Softmax is strictly increasing, so the kept set
+ * is the top-k by logit.  Order: larger score first, equal scores to the lower
+ * key index.  Scores are formed in float64.  With `parent` set this is the
+ * per-token candidate selection of the log-linear README (a selected coarse
+ * token's children become the candidates one level down).
+ *   q    device, float64 [batch][heads_q][q_len][head_dim]  (dtype must be F64)
+ *   k    device, float64 [batch][heads_kv][head_dim][keys]  (transposed means)
+ *   idx  device, int32 [batch][heads_q][rows][topk], each row ascending
+ *
+ * BASA_SELECT_CHANGE follows the LoSA post's locality pruning: per token, the
+ * mean over heads and channels of (q - k)^2, where q is the current and k the
+ * previous step's queries; the topk tokens with the largest change are active
+ * (ties to the lower token).
+ *   q, k device, [batch][heads_q][q_len][head_dim] of dtype (F32, BF16 or F64)
+ *   idx  device, int32 [batch][topk], ascending token numbers
+ *   (heads_kv, keys, rows, scale, q_rows and parent are ignored; q_len <= 1024)
+ *
+ * Errors: BASA_E_SHAPE for topk < 1 or topk above the candidate count,
+ * heads_q % heads_kv != 0, head_dim not a multiple of 8 or above 512,
+ * keys > 4096 (BLOCKS), parent_k*fanout > 4096, or non-positive scale.
+ */
+int basa_select(const basa_select_desc* desc, const void* q, const void* k, int dtype,
+                int32_t* idx, void* stream);
+
+/* One source of keys for basa_attn.  The key list of query tile t is the
+ * concatenation, over the descriptor's segments, of `count` entries of row
+ * (t >> shift) of the segment's index array; entry value e >= 0 names keys
+ * e*block_k .. e*block_k+block_k-1 of the segment's own key/value table, and
+ * a negative entry is an empty slot. */
+typedef struct basa_kv_segment {
+  const int32_t* idx; /* device int32; entry j of index row r of (b, h) is
+                         idx[((b*heads_q + h)*rows + r)*stride + j] */
+  const void* k;      /* device [batch][heads_kv][len][head_dim] of dtype */
+  const void* v;      /* device [batch][heads_kv][len][head_dim] of dtype */
+  int64_t len;        /* key rows per key head in k and v */
+  int64_t rows;       /* index rows per query head, >= ((lists-1) >> shift) + 1 */
+  int32_t count;      /* entries taken from each index row */
+  int32_t stride;     /* distance between index rows, in entries (>= count) */
+  int32_t shift;      /* query tile t reads index row t >> shift (0..30) */
+  int32_t dtype;      /* F32 or BF16 */
+  float bias;         /* added to every logit of this segment's keys */
+  int32_t reserved;
+} basa_kv_segment;
+
+#define BASA_MAX_SEGMENTS 4
+
+typedef struct basa_attn_desc {
+  int64_t batch;
+  int64_t heads_q;    /* query heads */
+  int64_t heads_kv;   /* key/value heads; query head h reads head h / (heads_q/heads_kv) */
+  int64_t len_q;      /* rows per query head in q, o and lse */
+  int64_t head_dim;   /* 64 or 128 */
+  int64_t lists;      /* query tiles (key lists) per query head */
+  int32_t tile_q;     /* query rows per tile (1..128) */
+  int32_t block_k;    /* keys per list entry (1..4096) */
+  int32_t n_segments; /* 1..BASA_MAX_SEGMENTS */
+  int32_t reserved;
+  basa_kv_segment seg[BASA_MAX_SEGMENTS];
+  /* q_rows: device int32 [batch][lists*tile_q] or NULL.  NULL: tile t holds
+     query rows t*tile_q .. t*tile_q+tile_q-1.  Otherwise its rows are
+     q_rows[b][t*tile_q + r]; they are read from q and written to o and lse,
+     and other rows of o and lse are left untouched (the LoSA cache update). */
+  const int32_t* q_rows;
+  double scale;       /* logit scale, normally 1/sqrt(head_dim) */
+} basa_attn_desc;
+
+/*
+ * basa_attn - attention confined to listed key blocks, with online softmax.
+ *
+ * Follows BA-Att section 2 (block-sparse attention: each query block attends
+ * only to the key/value blocks its mask keeps) with the softmax of Eq. 1
+ * restricted to those keys; bidirectional, no causal mask.  Segments express
+ * the log-linear README's KV enrichment (fine keys plus coarse candidates of
+ * every level, each level with logit bias l*ln(block)) and the LoSA prefix /
+ * in-block split.  For query row i: z_j = scale * q_i . k_j + bias(seg(j))
+ * over the listed keys j, LSE_i = ln sum_j exp(z_j),
+ * O_i = sum_j exp(z_j - LSE_i) v_j.  A row with no valid entry gets O = 0 and
+ * LSE = -inf.
+ *   q     device [batch][heads_q][len_q][head_dim] of q_dtype (F32 or BF16)
+ *   o     device [batch][heads_q][len_q][head_dim] of o_dtype (F32 or BF16)
+ *   lse   device float32 [batch][heads_q][len_q], natural logarithm
+ * Accumulation is float32.  On the MFMA path (bf16 q/k/v, head_dim 128,
+ * 128-row tiles, 128-key blocks, one segment) the probabilities are rounded
+ * to bf16 before the value product.  Entries must name existing keys:
+ * e*block_k + block_k <= len (not checked on the device).
+ * Errors: BASA_E_SHAPE for inconsistent sizes (including len_q not equal to
+ * lists*tile_q when q_rows is NULL), head_dim not 64/128, or a segment whose
+ * rows/count/stride/shift do not cover the tiles.
+ */
+int basa_attn(const basa_attn_desc* desc, const void* q, int q_dtype, void* o, int o_dtype,
+              float* lse, void* stream);
+
+/*
+ * basa_merge - combine two partial attention results of the same rows.
+ *
+ * Follows the LoSA post's prefix/suffix merge by online softmax: with
+ * m = max(lse_a, lse_b), LSE = m + ln(exp(lse_a - m) + exp(lse_b - m)) and
+ * O = exp(lse_a - LSE) o_a + exp(lse_b - LSE) o_b.  (anything, -inf) is the
+ * empty partial; two empty partials give O = 0, LSE = -inf.
+ *   o_a, o_b  device [rows][head_dim] of in_dtype (F32 or BF16)
+ *   lse_a/b   device float32 [rows]
+ *   o         device [rows][head_dim] of o_dtype (F32 or BF16); may be o_a
+ *             when o_dtype == in_dtype (in place)
+ *   lse       device float32 [rows]; may be lse_a
+ * Errors: BASA_E_SHAPE for rows < 0 or head_dim not a power of two in
+ * [8, 512]; BASA_E_UNSUPPORTED when o aliases an input of another dtype.
+ */
+int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse_a,
+               const void* o_b, const float* lse_b, int in_dtype, void* o, int o_dtype,
+               float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASA_H */

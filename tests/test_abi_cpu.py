@@ -1,0 +1,180 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/basa.h declares, and rejects invalid arguments with the documented
+status codes before any HIP call (so these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_mean_amd as basa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "basa.h")
+
+OK, NULLPTR, SHAPE, DTYPE, ALIGN, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(basa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("basa_pool", "basa_select", "basa_attn", "basa_merge"):
+        assert n in names
+    assert set(names) == set(basa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", basa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(basa_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(basa.lib, name)
+
+
+def test_status_strings_and_version():
+    for code in range(7):
+        assert basa.lib.basa_status_string(code)
+    assert basa.lib.basa_status_string(99) == b"unknown status"
+    assert basa.lib.basa_version() >= 100
+
+
+# a fake, aligned, never-dereferenced device address: validation fails before use
+FAKE = 1 << 20
+MISALIGNED = FAKE + 4
+
+
+def pool(x=FAKE, xdt=basa.BF16, outer=2, length=256, d=128, block=64, rows=FAKE, cols=None,
+         copy=None, cdt=basa.F32):
+    return basa.lib.basa_pool(x, xdt, outer, length, d, block, rows, cols, copy, cdt, None)
+
+
+def test_pool_validation():
+    assert pool(length=250) == SHAPE
+    assert pool(block=0) == SHAPE
+    assert pool(d=100) == SHAPE
+    assert pool(d=1024) == SHAPE
+    assert pool(outer=-1) == SHAPE
+    assert pool(xdt=7) == DTYPE
+    assert pool(copy=FAKE, cdt=basa.F64) == DTYPE
+    assert pool(x=None) == NULLPTR
+    assert pool(rows=None) == NULLPTR
+    assert pool(x=MISALIGNED) == ALIGN
+    assert pool(outer=0) == OK          # empty: nothing to do
+    assert pool(length=0) == OK
+
+
+def sel_desc(**kw):
+    d = basa.SelectDesc()
+    d.mode, d.topk, d.batch, d.heads_q, d.heads_kv = basa.SELECT_BLOCKS, 4, 1, 2, 2
+    d.q_len, d.rows, d.keys, d.head_dim, d.scale = 16, 16, 16, 64, 0.125
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def select(desc, q=FAKE, k=FAKE, dt=basa.F64, idx=FAKE):
+    return basa.lib.basa_select(ctypes.byref(desc), q, k, dt, idx, None)
+
+
+def test_select_validation():
+    assert basa.lib.basa_select(None, FAKE, FAKE, basa.F64, FAKE, None) == NULLPTR
+    assert select(sel_desc(topk=0)) == SHAPE
+    assert select(sel_desc(topk=17)) == SHAPE
+    assert select(sel_desc(heads_kv=3)) == SHAPE
+    assert select(sel_desc(keys=5000, topk=4)) == SHAPE
+    assert select(sel_desc(scale=0.0)) == SHAPE
+    assert select(sel_desc(scale=-1.0)) == SHAPE
+    assert select(sel_desc(rows=8)) == SHAPE            # rows != q_len without a row map
+    assert select(sel_desc(head_dim=60)) == SHAPE
+    assert select(sel_desc(), dt=basa.BF16) == DTYPE
+    assert select(sel_desc(mode=7)) == UNSUPPORTED
+    assert select(sel_desc(), q=None) == NULLPTR
+    assert select(sel_desc(), k=MISALIGNED) == ALIGN
+    assert select(sel_desc(batch=0)) == OK
+    # candidate restriction
+    assert select(sel_desc(parent=FAKE, parent_k=2, fanout=4, topk=9)) == SHAPE   # 9 > 2*4
+    assert select(sel_desc(parent=FAKE, parent_k=2, fanout=3)) == SHAPE           # 16 % 3
+    assert select(sel_desc(parent=FAKE, parent_k=2, fanout=4, q_rows=FAKE)) == UNSUPPORTED
+    # change mode
+    ch = sel_desc(mode=basa.SELECT_CHANGE, q_len=16, topk=5)
+    assert select(ch, dt=basa.BF16) != DTYPE
+    assert select(sel_desc(mode=basa.SELECT_CHANGE, q_len=16, topk=17), dt=basa.BF16) == SHAPE
+    assert select(sel_desc(mode=basa.SELECT_CHANGE, q_len=2000, topk=5), dt=basa.BF16) == SHAPE
+    assert select(ch, dt=9) == DTYPE
+
+
+def attn_desc(n_seg=1, **kw):
+    d = basa.AttnDesc()
+    d.batch, d.heads_q, d.heads_kv, d.len_q, d.head_dim = 1, 4, 2, 256, 128
+    d.lists, d.tile_q, d.block_k, d.n_segments, d.scale = 2, 128, 128, n_seg, 0.088
+    for i in range(n_seg):
+        g = d.seg[i]
+        g.idx, g.k, g.v, g.len, g.rows, g.count, g.stride = FAKE, FAKE, FAKE, 256, 2, 2, 2
+        g.dtype = basa.BF16
+    for k, v in kw.items():
+        if k.startswith("seg_"):
+            setattr(d.seg[0], k[4:], v)
+        else:
+            setattr(d, k, v)
+    return d
+
+
+def attn(desc, q=FAKE, qdt=basa.BF16, o=FAKE, odt=basa.BF16, lse=FAKE):
+    return basa.lib.basa_attn(ctypes.byref(desc), q, qdt, o, odt, lse, None)
+
+
+def test_attn_validation():
+    assert basa.lib.basa_attn(None, FAKE, 1, FAKE, 1, FAKE, None) == NULLPTR
+    assert attn(attn_desc(head_dim=96)) == SHAPE
+    assert attn(attn_desc(heads_kv=3)) == SHAPE
+    assert attn(attn_desc(lists=3)) == SHAPE            # 3*128 rows != len_q
+    assert attn(attn_desc(tile_q=0)) == SHAPE
+    assert attn(attn_desc(tile_q=256)) == SHAPE
+    assert attn(attn_desc(block_k=0)) == SHAPE
+    assert attn(attn_desc(n_seg=0)) == SHAPE
+    assert attn(attn_desc(n_seg=1, n_segments=5)) == SHAPE
+    assert attn(attn_desc(scale=float("inf"))) == SHAPE
+    assert attn(attn_desc(seg_count=-1)) == SHAPE
+    assert attn(attn_desc(seg_stride=1)) == SHAPE       # stride < count
+    assert attn(attn_desc(seg_rows=1)) == SHAPE         # 2 tiles need 2 index rows
+    assert attn(attn_desc(seg_shift=31)) == SHAPE
+    assert attn(attn_desc(seg_bias=float("nan"))) == SHAPE
+    assert attn(attn_desc(seg_dtype=basa.F64)) == DTYPE
+    assert attn(attn_desc(), qdt=basa.F64) == DTYPE
+    assert attn(attn_desc(), odt=basa.F64) == DTYPE
+    assert attn(attn_desc(), q=None) == NULLPTR
+    assert attn(attn_desc(seg_idx=None)) == NULLPTR
+    assert attn(attn_desc(), lse=None) == NULLPTR
+    assert attn(attn_desc(seg_v=MISALIGNED)) == ALIGN
+    assert attn(attn_desc(lists=0, len_q=0)) == OK
+    assert attn(attn_desc(batch=0)) == OK
+
+
+def merge(rows=8, d=128, oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, idt=basa.F32, o=FAKE,
+          odt=basa.BF16, lse=FAKE):
+    return basa.lib.basa_merge(rows, d, oa, la, ob, lb, idt, o, odt, lse, None)
+
+
+def test_merge_validation():
+    assert merge(rows=-1) == SHAPE
+    assert merge(d=96) == SHAPE
+    assert merge(d=4) == SHAPE
+    assert merge(idt=basa.F64) == DTYPE
+    assert merge(odt=basa.F64) == DTYPE
+    assert merge(ob=None) == NULLPTR
+    assert merge(o=MISALIGNED) == ALIGN
+    assert merge(o=FAKE, oa=FAKE, idt=basa.F32, odt=basa.BF16) == UNSUPPORTED   # aliasing, dtype change
+    assert merge(rows=0) == OK
+
+
+def test_binding_needs_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        basa.basa_pool(x, 16, mean_rows=torch.zeros(1, 1, 4, 64, dtype=torch.float64))

@@ -1,0 +1,340 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Indices must match bit for bit; O within 2e-2 and LSE within 1e-3 (max abs)
+for bf16 inputs with float32 accumulation, and tighter where the inputs are
+float32.  Attention tests take their key lists from the oracle's selection,
+never from the HIP path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from gpu_util import LSE_TOL, O_TOL, dev, host, max_err, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def basa():
+    assert torch.cuda.is_available(), "the GPU tests need a visible GPU"
+    import block_sparse_attention_mean_amd as mod
+    return mod
+
+
+def gpu_pool(basa, x, block, rows=True, cols=False, copy=None):
+    xt = dev(x)
+    *lead, length, d = xt.shape
+    nb = length // block
+    out_rows = torch.empty(*lead, nb, d, dtype=torch.float64, device="cuda") if rows else None
+    out_cols = torch.empty(*lead, d, nb, dtype=torch.float64, device="cuda") if cols else None
+    out_copy = torch.empty(*lead, nb, d, dtype=copy, device="cuda") if copy is not None else None
+    basa.basa_pool(xt, block, out_rows, out_cols, out_copy)
+    torch.cuda.synchronize()
+    return out_rows, out_cols, out_copy
+
+
+def gpu_select(basa, q, k, block, topk, scale):
+    """pool Q (rows) and K (transposed), then select: the BA-Att selection stage."""
+    qbar, _, _ = gpu_pool(basa, q, block)
+    _, kbt, _ = gpu_pool(basa, k, block, rows=False, cols=True)
+    b, h, nq, _ = qbar.shape
+    idx = torch.empty(b, h, nq, topk, dtype=torch.int32, device="cuda")
+    basa.basa_select(qbar, kbt, idx, topk, scale=scale)
+    torch.cuda.synchronize()
+    return host(idx)
+
+
+def oracle_select(q, k, block, topk, scale):
+    return orc.topk_ascending(orc.block_logits(orc.pool_mean(q, block), orc.pool_mean(k, block),
+                                               scale), topk)
+
+
+# --------------------------------------------------------------------------- pool
+
+def test_pool_bf16_exact_and_transposed(basa):
+    note("pool bf16 H4 L2048 d128 block128")
+    x = wl.make_dlm(11, heads=4, tokens=2048, head_dim=128)["q"]
+    r, c, _ = gpu_pool(basa, x, 128, rows=True, cols=True)
+    ref = orc.pool_mean(x, 128)
+    assert np.array_equal(host(r), ref)                 # exact: bf16 sums are exact in float64
+    assert np.array_equal(host(c), np.swapaxes(ref, -1, -2))
+
+
+def test_pool_f32_and_block_one(basa):
+    note("pool f32 tiny block64 / block1")
+    x = wl.make_tiny(5)["k"]
+    r, _, _ = gpu_pool(basa, x, 64)
+    ref = orc.pool_mean(x, 64)
+    assert max_err(host(r), ref) <= 1e-15 * np.abs(ref).max()
+    r1, _, _ = gpu_pool(basa, x, 1)
+    assert np.array_equal(host(r1), x.astype(np.float64))
+
+
+def test_pool_f64_levels_and_copies(basa):
+    note("pool f64 level input block16 d64 with f32/bf16 copies")
+    g = np.random.Generator(np.random.PCG64(12))
+    x = g.standard_normal((1, 3, 4096, 64))
+    r, _, c32 = gpu_pool(basa, x, 16, copy=torch.float32)
+    ref = orc.pool_mean(x, 16)
+    assert max_err(host(r), ref) <= 4e-16 * 16
+    assert np.array_equal(host(c32), ref.astype(np.float32).astype(np.float64))
+    _, _, c16 = gpu_pool(basa, x, 16, rows=False, copy=torch.bfloat16)
+    got = host(c16)
+    # nearest bf16: within half a bf16 ulp of the float64 mean
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(ref))) - 7)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-12))
+
+
+# --------------------------------------------------------------------------- select
+
+def test_select_tiny_planted_block(basa):
+    note("select tiny fp32 (planted block)")
+    w = wl.WORKLOADS["tiny"]
+    x = wl.generate("tiny")
+    got = gpu_select(basa, x["q"], x["k"], w.block, w.topk, w.scale)
+    ref = oracle_select(x["q"], x["k"], w.block, w.topk, w.scale)
+    assert np.array_equal(got, ref)
+    for h in range(w.heads):
+        assert wl.TINY_PLANT_KEY_BLOCK in got[0, h, wl.TINY_PLANT_QUERY_BLOCK]
+
+
+def test_select_ragged_rows_and_keys(basa):
+    note("select ragged: H3 rows37 keys100 top7 d64")
+    g = np.random.Generator(np.random.PCG64(14))
+    q = g.standard_normal((1, 3, 37 * 16, 64)).astype(np.float32)
+    k = g.standard_normal((1, 3, 100 * 16, 64)).astype(np.float32)
+    got = gpu_select(basa, q, k, 16, 7, 0.125)
+    assert np.array_equal(got, oracle_select(q, k, 16, 7, 0.125))
+
+
+def test_select_exact_ties_go_to_lower_index(basa):
+    note("select ties: duplicated key blocks and an all-zero query block")
+    g = np.random.Generator(np.random.PCG64(15))
+    q = g.standard_normal((1, 2, 20 * 16, 64)).astype(np.float32)
+    k = g.standard_normal((1, 2, 150 * 16, 64)).astype(np.float32)
+    k[:, :, 16 * 90:16 * 91] = k[:, :, 16 * 3:16 * 4]     # identical blocks -> equal scores
+    k[:, :, 16 * 120:16 * 121] = k[:, :, 16 * 3:16 * 4]
+    q[:, :, 0:16] = 0.0                                    # every score of row 0 ties at zero
+    q[:, 1, 16:32] = -0.0
+    for topk in (1, 5, 64, 150):
+        got = gpu_select(basa, q, k, 16, topk, 0.125)
+        ref = oracle_select(q, k, 16, topk, 0.125)
+        assert np.array_equal(got, ref), topk
+    assert np.array_equal(got[0, 0, 0], np.arange(150))
+
+
+def test_select_gqa_row_map_and_wide_rows(basa):
+    note("select GQA 8/2 heads, row map, 4096 keys (top-128)")
+    g = np.random.Generator(np.random.PCG64(16))
+    qf = g.standard_normal((1, 8, 16, 128))
+    kbar = g.standard_normal((1, 2, 4096, 128))
+    rows = np.array([[1, 4, 7, 10, 13]], dtype=np.int32)
+    idx = torch.empty(1, 8, 5, 128, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 128,
+                     scale=1 / math.sqrt(128), q_rows=dev(rows))
+    torch.cuda.synchronize()
+    ref = orc.topk_ascending(orc.block_logits(qf[:, :, rows[0]], kbar, 1 / math.sqrt(128)), 128)
+    assert np.array_equal(host(idx), ref)
+
+
+def test_select_children_of_parent_picks(basa):
+    note("select candidate mode: 256 rows, parent top-8 x fanout 16")
+    g = np.random.Generator(np.random.PCG64(17))
+    nq = nk = 256
+    q = g.standard_normal((1, 2, nq, 64))
+    kbar = g.standard_normal((1, 2, nk, 64))
+    parent = np.sort(np.stack([np.stack([g.choice(16, 8, replace=False) for _ in range(16)])
+                               for _ in range(2)])[None], axis=-1).astype(np.int32)
+    idx = torch.empty(1, 2, nq, 8, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(q), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 8,
+                     scale=0.125, parent=dev(parent), fanout=16)
+    torch.cuda.synchronize()
+    got = host(idx)
+    for h in range(2):
+        for a in range(nq):
+            cands = (parent[0, h, a // 16][:, None] * 16 + np.arange(16)).reshape(-1)
+            s = 0.125 * (kbar[0, h, cands] @ q[0, h, a])
+            assert np.array_equal(got[0, h, a], cands[orc.topk_ascending(s, 8)])
+
+
+def test_select_change_mode(basa):
+    note("select change mode: LoSA active tokens")
+    x = wl.make_losa(4, heads_q=32, heads_kv=8, prefix=256, head_dim=128)
+    idx = torch.empty(1, 5, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(x["q_cur"]), dev(x["q_prev"]), idx, 5, mode=basa.SELECT_CHANGE)
+    torch.cuda.synchronize()
+    ref = orc.active_tokens(x["q_cur"], x["q_prev"], 5)
+    assert np.array_equal(host(idx), ref)
+    assert host(idx).tolist() == [list(wl.LOSA_PLANTED)]
+    idx2 = torch.empty(1, 5, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(x["q_cur"]), dev(x["q_cur"]), idx2, 5, mode=basa.SELECT_CHANGE)
+    torch.cuda.synchronize()
+    assert host(idx2).tolist() == [[0, 1, 2, 3, 4]]    # all changes tie at zero
+
+
+def test_select_dlm16k_full(basa):
+    note("select dlm16k full: H32 L16384 block128 top64")
+    w = wl.WORKLOADS["dlm16k"]
+    x = wl.generate("dlm16k")
+    got = gpu_select(basa, x["q"], x["k"], w.block, w.topk, w.scale)
+    assert np.array_equal(got, oracle_select(x["q"], x["k"], w.block, w.topk, w.scale))
+
+
+# --------------------------------------------------------------------------- attention
+
+def run_attn(basa, q, segs, tile_q, block_k, scale, o_dtype, q_rows=None, o_init=None, lse_init=None):
+    """segs: list of (idx np, k np, v np, kwargs)."""
+    qt = dev(q)
+    segments = [basa.kv_segment(dev(i), dev(k), dev(v), **kw) for i, k, v, kw in segs]
+    o = (dev(o_init) if o_init is not None else
+         torch.zeros(qt.shape, dtype=o_dtype, device="cuda"))
+    lse = (dev(lse_init) if lse_init is not None else
+           torch.zeros(qt.shape[:3], dtype=torch.float32, device="cuda"))
+    basa.basa_attn(qt, segments, o, lse, tile_q=tile_q, block_k=block_k, scale=scale,
+                   q_rows=dev(q_rows) if q_rows is not None else None)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32])
+def test_attn_mfma_small_with_empty_slots(basa, o_dtype):
+    note(f"attn mfma H3 L1152 kept5 with empty slots, out {o_dtype}")
+    x = wl.make_dlm(21, heads=3, tokens=1152, head_dim=128)
+    g = np.random.Generator(np.random.PCG64(22))
+    nb = 9
+    idx = np.stack([np.stack([np.sort(g.choice(nb, 5, replace=False)) for _ in range(nb)])
+                    for _ in range(3)])[None].astype(np.int32)
+    idx[0, 0, 2, 1] = -1
+    idx[0, 2, 8, :] = -1                                   # an empty list
+    idx[0, 1, 4, 4] = -1
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, 1 / math.sqrt(128), o_dtype)
+    ro, rl = orc.sparse_attention(x["q"], x["k"], x["v"], idx, 128, 128, 1 / math.sqrt(128))
+    empty = np.zeros(ro.shape[:3], dtype=bool)
+    empty[0, 2, 8 * 128:] = True
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert max_err(o[~empty], ro[~empty]) <= O_TOL
+    assert max_err(lse[~empty], rl[~empty]) <= LSE_TOL
+
+
+def test_attn_mfma_dlm16k_sampled_and_deterministic(basa):
+    note("attn mfma dlm16k: oracle lists, 48 sampled tiles, repeat-run bitwise")
+    w = wl.WORKLOADS["dlm16k"]
+    x = wl.generate("dlm16k")
+    idx = oracle_select(x["q"], x["k"], w.block, w.topk, w.scale)
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, w.scale, torch.bfloat16)
+    o2, lse2 = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, w.scale, torch.bfloat16)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    g = np.random.Generator(np.random.PCG64(23))
+    lists = [(0, int(h), int(t)) for h, t in zip(g.integers(0, w.heads, 48), g.integers(0, w.blocks, 48))]
+    ro, rl = orc.sparse_attention(x["q"], x["k"], x["v"], idx, 128, 128, w.scale, lists=lists)
+    sel = ~np.isnan(rl)
+    assert max_err(o[sel], ro[sel]) <= O_TOL
+    assert max_err(lse[sel], rl[sel]) <= LSE_TOL
+
+
+def test_attn_generic_tiny_fp32(basa):
+    note("attn generic tiny fp32 full")
+    w = wl.WORKLOADS["tiny"]
+    x = wl.generate("tiny")
+    idx = oracle_select(x["q"], x["k"], w.block, w.topk, w.scale)
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 64, 64, w.scale, torch.float32)
+    ro, rl = orc.sparse_attention(x["q"], x["k"], x["v"], idx, 64, 64, w.scale)
+    assert max_err(o, ro) <= 1e-5
+    assert max_err(lse, rl) <= 1e-5
+
+
+def test_attn_generic_segments_bias_and_f32_tables(basa):
+    note("attn generic: 3 segments (bf16 fine + f32 coarse, shifts, level bias), d64 tile16")
+    g = np.random.Generator(np.random.PCG64(24))
+    n, d, blk = 1024, 64, 16
+    q = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
+    kf = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
+    vf = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
+    k1 = g.standard_normal((1, 2, 64, d)).astype(np.float32)
+    v1 = g.standard_normal((1, 2, 64, d)).astype(np.float32)
+    tiles = n // 16
+    i0 = np.sort(g.integers(0, n // blk, (1, 2, tiles, 8)), axis=-1).astype(np.int32)
+    i1 = np.sort(g.integers(0, 64 // blk, (1, 2, tiles >> 4, 3)), axis=-1).astype(np.int32)
+    i2 = np.zeros((1, 2, 1, 1), dtype=np.int32)
+    b1, b2 = math.log(16), 2 * math.log(16)
+    segs = [(i0, kf, vf, {}), (i1, k1, v1, {"shift": 4, "bias": b1}),
+            (i2, k1, v1, {"shift": 10, "bias": b2})]
+    o, lse = run_attn(basa, q, segs, 16, blk, 0.125, torch.float32)
+    # oracle: one table [fine | coarse] with per-entry bias
+    kt = np.concatenate([orc.as_f64(kf), k1.astype(np.float64)], axis=2)
+    vt = np.concatenate([orc.as_f64(vf), v1.astype(np.float64)], axis=2)
+    off = n // blk
+    full = np.concatenate([i0, np.repeat(i1, 16, axis=2) + off, np.repeat(i2, tiles, axis=2) + off], axis=-1)
+    bias = np.concatenate([np.zeros(i0.shape), np.full(i1.shape[:2] + (tiles, 3), b1),
+                           np.full(i2.shape[:2] + (tiles, 1), b2)], axis=-1)
+    ro, rl = orc.sparse_attention(q, kt, vt, full, 16, blk, 0.125, bias=np.repeat(bias, 1, axis=2))
+    assert max_err(o, ro) <= 1e-4
+    assert max_err(lse, rl) <= 1e-4
+
+
+def test_attn_generic_row_map_gqa_keeps_other_rows(basa):
+    note("attn generic: tile 1, q_rows, GQA 8/2, block16, top-8, in-place rows")
+    g = np.random.Generator(np.random.PCG64(25))
+    d = 128
+    q = wl.f32_to_bf16(g.standard_normal((1, 8, 16, d)).astype(np.float32))
+    k = wl.f32_to_bf16(g.standard_normal((1, 2, 1024, d)).astype(np.float32))
+    v = wl.f32_to_bf16(g.standard_normal((1, 2, 1024, d)).astype(np.float32))
+    rows = np.array([[1, 4, 7, 10, 13]], dtype=np.int32)
+    idx = np.sort(np.stack([np.stack([g.choice(64, 8, replace=False) for _ in range(5)])
+                            for _ in range(8)])[None], axis=-1).astype(np.int32)
+    o0 = g.standard_normal((1, 8, 16, d)).astype(np.float32)
+    l0 = g.standard_normal((1, 8, 16)).astype(np.float32)
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 1, 16, 1 / math.sqrt(d), torch.float32,
+                      q_rows=rows, o_init=o0, lse_init=l0)
+    ro, rl = orc.sparse_attention(q, k, v, idx, 1, 16, 1 / math.sqrt(d), q_rows=rows)
+    act = np.zeros((1, 8, 16), dtype=bool)
+    act[:, :, rows[0]] = True
+    assert max_err(o[act], ro[act]) <= 1e-4 and max_err(lse[act], rl[act]) <= 1e-4
+    assert np.array_equal(o[~act], o0[~act].astype(np.float64))
+    assert np.array_equal(lse[~act], l0[~act].astype(np.float64))
+
+
+# --------------------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("in_dt,out_dt", [(torch.float32, torch.bfloat16), (torch.bfloat16, torch.float32),
+                                          (torch.float32, torch.float32)])
+def test_merge_matches_oracle(basa, in_dt, out_dt):
+    note(f"merge {in_dt}->{out_dt}")
+    g = np.random.Generator(np.random.PCG64(26))
+    rows, d = 1000, 128
+    oa = g.standard_normal((rows, d)).astype(np.float32)
+    ob = g.standard_normal((rows, d)).astype(np.float32)
+    la = (3 * g.standard_normal(rows)).astype(np.float32)
+    lb = (3 * g.standard_normal(rows)).astype(np.float32)
+    la[:10] = -np.inf
+    lb[5:15] = -np.inf                                  # rows 5..9 are empty on both sides
+    if in_dt == torch.bfloat16:
+        oa, ob = wl.bf16_to_f32(wl.f32_to_bf16(oa)), wl.bf16_to_f32(wl.f32_to_bf16(ob))
+    toa, tob = dev(oa).to(in_dt), dev(ob).to(in_dt)
+    o = torch.empty(rows, d, dtype=out_dt, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    basa.basa_merge(toa, dev(la), tob, dev(lb), o, lse)
+    torch.cuda.synchronize()
+    ro, rl = orc.merge(oa, la, ob, lb)
+    tol = 2e-2 if out_dt == torch.bfloat16 else 1e-5
+    assert max_err(host(o), ro) <= tol
+    assert max_err(host(lse), rl) <= 1e-5
+    assert np.all(host(o)[5:10] == 0) and np.all(np.isneginf(host(lse)[5:10]))
+
+
+def test_merge_in_place(basa):
+    note("merge in place f32")
+    g = np.random.Generator(np.random.PCG64(27))
+    oa = g.standard_normal((300, 64)).astype(np.float32)
+    ob = g.standard_normal((300, 64)).astype(np.float32)
+    la = g.standard_normal(300).astype(np.float32)
+    lb = g.standard_normal(300).astype(np.float32)
+    toa, tla = dev(oa), dev(la)
+    basa.basa_merge(toa, tla, dev(ob), dev(lb), toa, tla)
+    torch.cuda.synchronize()
+    ro, rl = orc.merge(oa, la, ob, lb)
+    assert max_err(host(toa), ro) <= 1e-5 and max_err(host(tla), rl) <= 1e-5
