@@ -40,7 +40,20 @@ def parse():
     p.add_argument("--workload", default="dlm64k", choices=["dlm64k", "dlm16k"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stages", action="store_true", help="skip the merge stage measurement")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run a device-to-device copy of BYTES bytes 5 times (calibrates the "
+                        "HBM byte counters of a profiler run) and exit")
     return p.parse_args()
+
+
+def copy_probe(nbytes: int) -> None:
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": 5}))
 
 
 def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
@@ -78,6 +91,9 @@ def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by "
               "(batch, head) with no exchange, so N GPUs run N independent copies.", file=sys.stderr)

@@ -7,29 +7,42 @@
 // the kept blocks, and the kernel emits O and the natural-log LSE.
 //
 // Work decomposition
-//   one workgroup = one query tile (b, h, 128 rows), 4 waves x 32 rows.
-//   For each kept key block: K (128 x 128) and V (transposed, 128 x 128) are
-//   staged in LDS; every wave computes S^T = K Q^T for its 32 rows with
-//   v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held
-//   in registers for the whole walk), so each lane holds 64 logits of ONE
-//   query row: the row max and row sum need only one cross-lane step (lane
-//   l and l^32).  Then O^T += V^T P^T with the same instruction (A = V^T from
-//   LDS, B = P straight from the S accumulators after a bf16 conversion).
+//   One workgroup (8 waves) computes one query tile of 128 rows and owns a CU.
+//   Waves 0-3 take keys 0-63 of every kept block, waves 4-7 keys 64-127, each
+//   for query rows 32*(w%4) .. +31; the two halves' softmax states are merged
+//   through LDS at the end.  Two waves per SIMD let one wave's softmax overlap
+//   the other's MFMA.
+//   For each block a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+//   (A = K rows from LDS, B = the wave's Q rows, held in registers for the
+//   whole walk), so each lane holds 32 logits of ONE query row: the row max and
+//   row sum need one cross-lane step (lane l and l^32).  Then O^T += V^T P^T
+//   with the same instruction (A = V^T from LDS, B = P taken straight from the
+//   S accumulators after a bf16 conversion).
 //
-// Key permutation.  The 32x32 accumulator puts row rho of S^T at register
+// Key permutation.  The 32x32 accumulator puts row rho of S^T in register
 // r = 4*(rho/8) + rho%4 of lane-half (rho/4)%2.  Loading key kappa into MFMA
 // row rho = kappa with bits 2 and 3 swapped makes registers 8c..8c+7 of lane
 // half h hold keys 16c + 8h .. 16c + 8h + 7, which is exactly the B-operand
-// layout of a 16-key P chunk.  The V^T operand reads the same keys, so the
-// contraction pairs each P value with its own V row.
+// layout of a 16-key P chunk; the V^T operand reads the same keys.
 //
-// LDS rows are padded to 272 bytes so that the 16-byte reads of 16 lanes fall
-// in distinct banks.  Two workgroups fit per CU (2 x 68 KB of 160 KB), which
-// gives each SIMD two waves to overlap one wave's softmax with the other's MFMA.
+// Data movement (double-buffered, one barrier per block)
+//   K: direct global->LDS loads (global_load_lds_dwordx4), 16 bytes per lane,
+//      rows of 256 bytes whose 16-byte chunks are XOR-swizzled by the row
+//      number, so the 16 lanes that read one MFMA operand hit distinct banks.
+//   V: loaded one block ahead into registers (4 keys x 8 channels per thread)
+//      and written transposed (channel-major, rows padded to 272 bytes) into
+//      the other buffer while the current block computes.
 //
-// Workgroups are numbered so that each XCD (dispatch round-robins workgroups
-// over the 8 XCDs) receives a contiguous run of tiles: neighbouring query
-// tiles of the same head, whose kept key blocks overlap, share that XCD's L2.
+// Softmax: log2 domain with the scale folded in; the running max is only
+// raised when a block's max exceeds it by more than 8 (a factor 256), so the
+// O rescale is usually skipped; O/l and LSE = m + log2(l) are unchanged by the
+// choice of m.
+//
+// Workgroup numbering: dispatch hands workgroups to the 8 XCDs round-robin.
+// Tiles are numbered so that in every round of 8 x 32 resident workgroups all
+// XCDs work on one contiguous run of tiles (the same head), each XCD on its
+// own contiguous sub-run: the head's K/V stays in the shared last-level cache
+// and neighbouring query tiles, whose kept blocks overlap, share an L2.
 #include "common.h"
 
 namespace basa {
@@ -38,9 +51,13 @@ namespace {
 constexpr int D = 128;
 constexpr int BQ = 128;
 constexpr int BK = 128;
-constexpr int KSTR = D * 2 + 16;   // bytes per K row in LDS
-constexpr int VSTR = BK * 2 + 16;  // bytes per V^T row (one channel) in LDS
-constexpr int LDS_BYTES = BK * KSTR + D * VSTR;
+constexpr int NT = 512;                       // threads per workgroup (8 waves)
+constexpr int KBUF = BK * D * 2;              // 32 KB, swizzled rows of 256 B
+constexpr int VSTR = BK * 2 + 16;             // bytes per V^T row (one channel)
+constexpr int VBUF = D * VSTR;                // 34 KB
+constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF;
+constexpr int RESIDENT_PER_XCD = 32;          // one workgroup per CU, 32 CUs per XCD
+constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
 
 struct MfmaArgs {
   const uint16_t* q;
@@ -58,16 +75,75 @@ __device__ __forceinline__ int swap_bits_2_3(int x) {
   return (x & ~0xC) | ((x >> 1) & 0x4) | ((x << 1) & 0x8);
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
-  uint8_t* ks = smem;
-  uint8_t* vts = smem + BK * KSTR;
+__device__ __forceinline__ int64_t tile_of(int64_t w, int64_t tiles) {
+  const int64_t round_sz = 8 * RESIDENT_PER_XCD;
+  const int64_t full = (tiles / round_sz) * round_sz;
+  if (w >= full) return w;
+  const int64_t xcd = w % 8, k = w / 8;
+  const int64_t r = k / RESIDENT_PER_XCD, s = k % RESIDENT_PER_XCD;
+  return r * round_sz + xcd * RESIDENT_PER_XCD + s;
+}
 
-  // XCD-aware tile numbering (bijective: the tail beyond a multiple of 8 keeps its id)
-  const int64_t w = blockIdx.x;
-  const int64_t full = (a.tiles / 8) * 8;
-  const int64_t tile = (w < full) ? (w % 8) * (a.tiles / 8) + w / 8 : w;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// K block -> LDS: wave w issues 4 DMA loads of 1 KB (4 rows each); lane l of
+// load i lands at byte 16*l of row group (4w+i), i.e. row r = 4*(4w+i) + l/16,
+// physical chunk p = l%16, and fetches logical chunk p ^ (r & 15) of that row.
+__device__ __forceinline__ void load_k_async(uint8_t* kbuf, const uint16_t* kg, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int grp = wave * 4 + i;
+    const int r = grp * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const uint16_t* src = kg + r * D + c * 8;
+    uint8_t* dst = kbuf + grp * 1024;  // wave-uniform base; the lane offset is implicit
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  }
+}
+
+struct VRegs {
+  uint4 r0, r1, r2, r3;
+};
+
+// V block -> registers: thread t loads keys 4*(t%32) .. +3, channels 8*(t/32) .. +7.
+__device__ __forceinline__ VRegs load_v(const uint16_t* vg, int tid) {
+  const int kgrp = tid & 31, dg = tid >> 5;
+  const uint16_t* p = vg + (4 * kgrp) * D + dg * 8;
+  VRegs v;
+  v.r0 = *reinterpret_cast<const uint4*>(p);
+  v.r1 = *reinterpret_cast<const uint4*>(p + D);
+  v.r2 = *reinterpret_cast<const uint4*>(p + 2 * D);
+  v.r3 = *reinterpret_cast<const uint4*>(p + 3 * D);
+  return v;
+}
+
+__device__ __forceinline__ void store_vt(uint8_t* vbuf, const VRegs& v, int tid) {
+  const int kgrp = tid & 31, dg = tid >> 5;
+  const uint32_t w0[4] = {v.r0.x, v.r0.y, v.r0.z, v.r0.w};
+  const uint32_t w1[4] = {v.r1.x, v.r1.y, v.r1.z, v.r1.w};
+  const uint32_t w2[4] = {v.r2.x, v.r2.y, v.r2.z, v.r2.w};
+  const uint32_t w3[4] = {v.r3.x, v.r3.y, v.r3.z, v.r3.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // channel 8*dg + 2j from the low halves, 8*dg + 2j + 1 from the high halves
+    uint2 lo, hv;
+    lo.x = (w0[j] & 0xFFFFu) | (w1[j] << 16);
+    lo.y = (w2[j] & 0xFFFFu) | (w3[j] << 16);
+    hv.x = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
+    hv.y = (w2[j] >> 16) | (w3[j] & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j) * VSTR + 8 * kgrp) = lo;
+    *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j + 1) * VSTR + 8 * kgrp) = hv;
+  }
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // buffer i of K at smem + i*KBUF, of V^T at smem + 2*KBUF + i*VBUF
+
+  const int64_t tile = tile_of(blockIdx.x, a.tiles);
   const int64_t t = tile % a.lists;
   const int64_t bh = tile / a.lists;
   const int h = (int)(bh % a.heads_q);
@@ -76,12 +152,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave & 3;     // row group: query rows 32*rw .. +31
+  const int half = wave >> 2;  // key half: keys 64*half .. +63 of each block
   const int li = lane & 31;
   const int hi = lane >> 5;
 
-  // this lane's query row and its 128 channels as 8 B-operand fragments
-  const int64_t qrow = t * BQ + wave * 32 + li;
+  const int64_t qrow = t * BQ + rw * 32 + li;
   const uint16_t* qp = a.q + ((b * a.heads_q + h) * a.len_q + qrow) * D;
   bf16x8 qf[8];
 #pragma unroll
@@ -92,122 +169,140 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[u][r] = 0.f;
-  float m = -INFINITY;  // running row max of scale*log2(e)*logit
-  float l = 0.f;        // this lane's half of the running row sum
+  float m = -INFINITY;  // running row max of scale*log2(e)*logit (lazily raised)
+  float l = 0.f;        // this lane's share of the running row sum
 
   const int32_t* lst = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
   const uint16_t* kbase = a.k + (b * a.heads_kv + hk) * a.len_k * D;
   const uint16_t* vbase = a.v + (b * a.heads_kv + hk) * a.len_k * D;
-  const int krow_lds = swap_bits_2_3(li);
+  const int krow_l = swap_bits_2_3(li);
+  const int nblk_k = (int)(a.len_k / BK);
 
-  for (int e = 0; e < a.kept; ++e) {
-    const int blk = lst[e];
-    if (blk < 0 || (int64_t)blk * BK + BK > a.len_k) continue;  // empty slot (or out of range)
-    const uint16_t* kg = kbase + (int64_t)blk * BK * D;
-    const uint16_t* vg = vbase + (int64_t)blk * BK * D;
+  // find the first valid entry (empty or out-of-range slots are skipped)
+  int e = 0;
+  int blk = -1;
+  for (; e < a.kept; ++e) {
+    blk = lst[e];
+    if (blk >= 0 && blk < nblk_k) break;
+  }
+  int buf = 0;
+  if (e < a.kept) {
+    load_k_async(smem, kbase + (int64_t)blk * BK * D, wave, lane);
+    const VRegs v0 = load_v(vbase + (int64_t)blk * BK * D, tid);
+    wait_vm_all();
+    store_vt(smem + 2 * KBUF, v0, tid);
+  }
+  __syncthreads();
 
-    // global -> registers (K: 8 x 16 B per thread; V: 2 x 4 rows x 16 B per thread)
-    uint4 kr[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ch = tid + 256 * i;
-      kr[i] = *reinterpret_cast<const uint4*>(kg + (ch >> 4) * D + (ch & 15) * 8);
+  while (e < a.kept) {
+    // next valid entry
+    int e_next = e + 1;
+    int blk_next = -1;
+    for (; e_next < a.kept; ++e_next) {
+      blk_next = lst[e_next];
+      if (blk_next >= 0 && blk_next < nblk_k) break;
     }
-    const int kgrp = tid & 31;
-    uint4 vr[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dg = (tid >> 5) + 8 * i;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[i][r] = *reinterpret_cast<const uint4*>(vg + (4 * kgrp + r) * D + dg * 8);
+    const bool has_next = e_next < a.kept;
+    VRegs vn;
+    if (has_next) {
+      load_k_async(smem + (buf ^ 1) * KBUF, kbase + (int64_t)blk_next * BK * D, wave, lane);
+      vn = load_v(vbase + (int64_t)blk_next * BK * D, tid);
     }
-    __syncthreads();  // previous block's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ch = tid + 256 * i;
-      *reinterpret_cast<uint4*>(ks + (ch >> 4) * KSTR + (ch & 15) * 16) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dg = (tid >> 5) + 8 * i;
-      const uint32_t w0[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-      const uint32_t w1[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-      const uint32_t w2[4] = {vr[i][2].x, vr[i][2].y, vr[i][2].z, vr[i][2].w};
-      const uint32_t w3[4] = {vr[i][3].x, vr[i][3].y, vr[i][3].z, vr[i][3].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // channel 8*dg + 2j (low halves) and 8*dg + 2j + 1 (high halves)
-        uint2 lo, hv;
-        lo.x = (w0[j] & 0xFFFFu) | (w1[j] << 16);
-        lo.y = (w2[j] & 0xFFFFu) | (w3[j] << 16);
-        hv.x = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
-        hv.y = (w2[j] >> 16) | (w3[j] & 0xFFFF0000u);
-        *reinterpret_cast<uint2*>(vts + (8 * dg + 2 * j) * VSTR + 8 * kgrp) = lo;
-        *reinterpret_cast<uint2*>(vts + (8 * dg + 2 * j + 1) * VSTR + 8 * kgrp) = hv;
-      }
-    }
-    __syncthreads();
 
-    // S^T = K Q^T for 4 sub-tiles of 32 keys
-    f32x16 s[4];
+    // S^T = K Q^T for this wave's two 32-key sub-tiles
+    const uint8_t* kcur = smem + buf * KBUF;
+    f32x16 s[2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
-      const uint8_t* krow = ks + (32 * st + krow_lds) * KSTR + 16 * hi;
+      const int krow = 64 * half + 32 * st + krow_l;
+      const uint8_t* rowp = kcur + krow * 256;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 32 * c);
+        const int chunk = (2 * c + hi) ^ (krow & 15);
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(rowp + chunk * 16);
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], s[st], 0, 0, 0);
       }
     }
 
-    // online softmax (log2 domain); lane halves l and l^32 share a row
-    float mx = s[0][0];
+    // online softmax in the log2 domain; lanes l and l^32 hold the same row
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * a.scale_log2);
-    const float alpha = exp2f(m - m_new);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__ballot(mx > m + kLazy) != 0) {  // some row outgrew its max: rescale (wave-uniform)
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+      m = m_new;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(__builtin_fmaf(s[st][r], a.scale_log2, -m_new));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], a.scale_log2, -m));
         s[st][r] = p;
         psum += p;
       }
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+    l += psum;
 
-    // O^T += V^T P^T, 16 keys per step
+    if (has_next) {
+      wait_vm_all();  // K DMA into the other buffer and the V registers have landed
+      store_vt(smem + 2 * KBUF + (buf ^ 1) * VBUF, vn, tid);
+    }
+
+    // O^T += V^T P^T over this wave's 64 keys, 16 at a time
+    const uint8_t* vcur = smem + 2 * KBUF + buf * VBUF;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         bf16x8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[st][8 * cc + j];
-        const int key0 = 32 * st + 16 * cc + 8 * hi;
+        const int key0 = 64 * half + 32 * st + 16 * cc + 8 * hi;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vts + (32 * u + li) * VSTR + 2 * key0);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vcur + (32 * u + li) * VSTR + 2 * key0);
           oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[u], 0, 0, 0);
         }
       }
     }
+    __syncthreads();  // the current buffers are free; the next ones are complete
+    buf ^= 1;
+    e = e_next;
+    blk = blk_next;
   }
 
-  // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l + __shfl_xor(l, 32);
+  // merge the two key halves: waves 4-7 hand (m, l, O) to waves 0-3 through LDS
+  float* xo = reinterpret_cast<float*>(smem);                     // [4 waves][64 regs][64 lanes]
+  float* xm = reinterpret_cast<float*>(smem + 4 * 64 * 64 * 4);  // [4 waves][64 lanes]
+  float* xl = xm + 4 * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(rw * 64 + u * 16 + r) * 64 + lane] = oacc[u][r];
+    xm[rw * 64 + lane] = m;
+    xl[rw * 64 + lane] = l;
+  }
+  __syncthreads();
+  if (half == 1) return;
+  const float m2 = xm[rw * 64 + lane];
+  const float l2 = xl[rw * 64 + lane];
+  const float mm = fmaxf(m, m2);
+  const float f1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+  const float lane_l = l * f1 + l2 * f2;
+  const float l_tot = lane_l + __shfl_xor(lane_l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = (b * a.heads_q + h) * a.len_q + qrow;
 #pragma unroll
@@ -215,19 +310,24 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int ch = 32 * u + 8 * rq + 4 * hi;
-      const float v0 = oacc[u][4 * rq + 0] * inv, v1 = oacc[u][4 * rq + 1] * inv;
-      const float v2 = oacc[u][4 * rq + 2] * inv, v3 = oacc[u][4 * rq + 3] * inv;
+      float vv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * rq + j;
+        vv[j] = (oacc[u][r] * f1 + xo[(rw * 64 + u * 16 + r) * 64 + lane] * f2) * inv;
+      }
       if constexpr (OUT_BF16) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+        pk.x = (uint32_t)f32_to_bf16_bits(vv[0]) | ((uint32_t)f32_to_bf16_bits(vv[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(vv[2]) | ((uint32_t)f32_to_bf16_bits(vv[3]) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + orow * D + ch) = pk;
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow * D + ch) = make_float4(v0, v1, v2, v3);
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow * D + ch) =
+            make_float4(vv[0], vv[1], vv[2], vv[3]);
       }
     }
   }
-  if (hi == 0) a.lse[orow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (hi == 0) a.lse[orow] = l_tot > 0.f ? (mm + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -262,11 +362,15 @@ hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int
   a.kept = g.count;
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
   if (a.tiles == 0) return hipSuccess;
+  const void* fn = o_dtype == BASA_BF16 ? (const void*)attn_mfma_kernel<true>
+                                        : (const void*)attn_mfma_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)a.tiles);
   if (o_dtype == BASA_BF16)
-    attn_mfma_kernel<true><<<grid, 256, 0, s>>>(a);
+    attn_mfma_kernel<true><<<grid, NT, LDS_BYTES, s>>>(a);
   else
-    attn_mfma_kernel<false><<<grid, 256, 0, s>>>(a);
+    attn_mfma_kernel<false><<<grid, NT, LDS_BYTES, s>>>(a);
   return hipGetLastError();
 }
 
