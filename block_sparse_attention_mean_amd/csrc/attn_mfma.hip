@@ -26,12 +26,15 @@
 // layout of a 16-key P chunk; the V^T operand reads the same keys.
 //
 // Data movement (double-buffered, one barrier per block)
-//   K: direct global->LDS loads (global_load_lds_dwordx4), 16 bytes per lane,
-//      rows of 256 bytes whose 16-byte chunks are XOR-swizzled by the row
-//      number, so the 16 lanes that read one MFMA operand hit distinct banks.
-//   V: loaded one block ahead into registers (4 keys x 8 channels per thread)
-//      and written transposed (channel-major, rows padded to 272 bytes) into
-//      the other buffer while the current block computes.
+//   K and V of the next block are loaded into registers at the top of an
+//   iteration and written to the other LDS buffer after the current block's
+//   softmax, so the loads overlap the current block's MFMA and softmax work.
+//   (Direct global->LDS loads were tried: the compiler cannot prove that the
+//   DMA into one buffer does not alias reads of the other and waits for the
+//   loads before every LDS read, exposing the full memory latency.)
+//   K rows are 256 bytes whose 16-byte chunks are XOR-swizzled by the row
+//   number, so the 16 lanes that read one MFMA operand hit distinct banks;
+//   V is stored transposed (channel-major, rows padded to 272 bytes).
 //
 // Softmax: log2 domain with the scale folded in; the running max is only
 // raised when a block's max exceeds it by more than 8 (a factor 256), so the
@@ -55,7 +58,8 @@ constexpr int NT = 512;                       // threads per workgroup (8 waves)
 constexpr int KBUF = BK * D * 2;              // 32 KB, swizzled rows of 256 B
 constexpr int VSTR = BK * 2 + 16;             // bytes per V^T row (one channel)
 constexpr int VBUF = D * VSTR;                // 34 KB
-constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF;
+constexpr int MAX_KEPT = 4096;                // list entries staged in LDS
+constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF + MAX_KEPT * 4;
 constexpr int RESIDENT_PER_XCD = 32;          // one workgroup per CU, 32 CUs per XCD
 constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
 
@@ -84,21 +88,30 @@ __device__ __forceinline__ int64_t tile_of(int64_t w, int64_t tiles) {
   return r * round_sz + xcd * RESIDENT_PER_XCD + s;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+struct KRegs {
+  uint4 r0, r1, r2, r3;
+};
 
-// K block -> LDS: wave w issues 4 DMA loads of 1 KB (4 rows each); lane l of
-// load i lands at byte 16*l of row group (4w+i), i.e. row r = 4*(4w+i) + l/16,
-// physical chunk p = l%16, and fetches logical chunk p ^ (r & 15) of that row.
-__device__ __forceinline__ void load_k_async(uint8_t* kbuf, const uint16_t* kg, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int grp = wave * 4 + i;
-    const int r = grp * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    const uint16_t* src = kg + r * D + c * 8;
-    uint8_t* dst = kbuf + grp * 1024;  // wave-uniform base; the lane offset is implicit
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-  }
+// K block -> registers: thread t loads 16-byte chunks t, t+512, t+1024, t+1536
+// (row = chunk/16, logical chunk = chunk%16).
+__device__ __forceinline__ KRegs load_k(const uint16_t* kg, int tid) {
+  const uint16_t* p = kg + (tid >> 4) * D + (tid & 15) * 8;
+  KRegs k;
+  k.r0 = *reinterpret_cast<const uint4*>(p);
+  k.r1 = *reinterpret_cast<const uint4*>(p + 32 * D);
+  k.r2 = *reinterpret_cast<const uint4*>(p + 64 * D);
+  k.r3 = *reinterpret_cast<const uint4*>(p + 96 * D);
+  return k;
+}
+
+// registers -> swizzled K rows: logical chunk c of row r sits at physical chunk c ^ (r & 15)
+__device__ __forceinline__ void store_k(uint8_t* kbuf, const KRegs& k, int tid) {
+  const int r = tid >> 4, c = tid & 15;
+  const int off = r * 256 + ((c ^ (r & 15)) * 16);  // rows r+32i keep the same r & 15
+  *reinterpret_cast<uint4*>(kbuf + off) = k.r0;
+  *reinterpret_cast<uint4*>(kbuf + off + 32 * 256) = k.r1;
+  *reinterpret_cast<uint4*>(kbuf + off + 64 * 256) = k.r2;
+  *reinterpret_cast<uint4*>(kbuf + off + 96 * 256) = k.r3;
 }
 
 struct VRegs {
@@ -126,17 +139,16 @@ __device__ __forceinline__ void store_vt(uint8_t* vbuf, const VRegs& v, int tid)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // channel 8*dg + 2j from the low halves, 8*dg + 2j + 1 from the high halves
+    // v_perm_b32 selects bytes of {a:b}: 0x05040100 = low halves (b, a), 0x07060302 = high halves
     uint2 lo, hv;
-    lo.x = (w0[j] & 0xFFFFu) | (w1[j] << 16);
-    lo.y = (w2[j] & 0xFFFFu) | (w3[j] << 16);
-    hv.x = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
-    hv.y = (w2[j] >> 16) | (w3[j] & 0xFFFF0000u);
+    lo.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
+    hv.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
+    hv.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u);
     *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j) * VSTR + 8 * kgrp) = lo;
     *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j + 1) * VSTR + 8 * kgrp) = hv;
   }
 }
-
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
@@ -163,6 +175,10 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
   bf16x8 qf[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hi);
+  // settle the Q loads here (a compiler-visible vmcnt(0)): otherwise the
+  // wait-count bookkeeping at the loop head cannot tell them from the in-loop
+  // prefetches and makes every block wait for the next block's loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -172,7 +188,13 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
   float m = -INFINITY;  // running row max of scale*log2(e)*logit (lazily raised)
   float l = 0.f;        // this lane's share of the running row sum
 
-  const int32_t* lst = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
+  // the tile's key list, staged in LDS once (after the K/V buffers)
+  int32_t* lst = reinterpret_cast<int32_t*>(smem + 2 * KBUF + 2 * VBUF);
+  {
+    const int32_t* g = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
+    for (int i = tid; i < a.kept; i += NT) lst[i] = g[i];
+  }
+  __syncthreads();
   const uint16_t* kbase = a.k + (b * a.heads_kv + hk) * a.len_k * D;
   const uint16_t* vbase = a.v + (b * a.heads_kv + hk) * a.len_k * D;
   const int krow_l = swap_bits_2_3(li);
@@ -187,9 +209,9 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
   }
   int buf = 0;
   if (e < a.kept) {
-    load_k_async(smem, kbase + (int64_t)blk * BK * D, wave, lane);
+    const KRegs k0 = load_k(kbase + (int64_t)blk * BK * D, tid);
     const VRegs v0 = load_v(vbase + (int64_t)blk * BK * D, tid);
-    wait_vm_all();
+    store_k(smem, k0, tid);
     store_vt(smem + 2 * KBUF, v0, tid);
   }
   __syncthreads();
@@ -203,9 +225,10 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
       if (blk_next >= 0 && blk_next < nblk_k) break;
     }
     const bool has_next = e_next < a.kept;
+    KRegs kn;
     VRegs vn;
     if (has_next) {
-      load_k_async(smem + (buf ^ 1) * KBUF, kbase + (int64_t)blk_next * BK * D, wave, lane);
+      kn = load_k(kbase + (int64_t)blk_next * BK * D, tid);
       vn = load_v(vbase + (int64_t)blk_next * BK * D, tid);
     }
 
@@ -218,12 +241,14 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
       for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
       const int krow = 64 * half + 32 * st + krow_l;
       const uint8_t* rowp = kcur + krow * 256;
+      bf16x8 af[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int chunk = (2 * c + hi) ^ (krow & 15);
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(rowp + chunk * 16);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], s[st], 0, 0, 0);
-      }
+      for (int c = 0; c < 8; ++c)
+        af[c] = *reinterpret_cast<const bf16x8*>(rowp + (((2 * c + hi) ^ (krow & 15)) * 16));
+      __builtin_amdgcn_sched_barrier(0);  // all 8 operand reads in flight before the chain
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c], qf[c], s[st], 0, 0, 0);
     }
 
     // online softmax in the log2 domain; lanes l and l^32 hold the same row
@@ -254,8 +279,8 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
       }
     l += psum;
 
-    if (has_next) {
-      wait_vm_all();  // K DMA into the other buffer and the V registers have landed
+    if (has_next) {  // the next block's buffers were last read before the previous barrier
+      store_k(smem + (buf ^ 1) * KBUF, kn, tid);
       store_vt(smem + 2 * KBUF + (buf ^ 1) * VBUF, vn, tid);
     }
 
@@ -337,6 +362,7 @@ bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype) {
   return q_dtype == BASA_BF16 && d->n_segments == 1 && g.dtype == BASA_BF16 && g.shift == 0 &&
          g.bias == 0.f && d->head_dim == D && d->tile_q == BQ && d->block_k == BK &&
          d->q_rows == nullptr && d->lists * BQ == d->len_q && d->scale > 0.0 &&
+         g.count <= MAX_KEPT &&
          (o_dtype == BASA_BF16 || o_dtype == BASA_F32);
 }
 
