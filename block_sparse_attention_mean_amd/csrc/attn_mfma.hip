@@ -7,12 +7,12 @@
 // the kept blocks, and the kernel emits O and the natural-log LSE.
 //
 // Work decomposition
-//   One workgroup (8 waves) computes one query tile of 128 rows and owns a CU.
-//   Waves 0-3 take keys 0-63 of every kept block, waves 4-7 keys 64-127, each
-//   for query rows 32*(w%4) .. +31; the two halves' softmax states are merged
-//   through LDS at the end.  Two waves per SIMD let one wave's softmax overlap
-//   the other's MFMA.
-//   For each block a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+//   One workgroup (4 waves) computes one query tile of 128 rows; wave w owns
+//   rows 32w .. 32w+31.  Kept key blocks are streamed in stages of 64 keys
+//   (two stages per block).  Two workgroups share a CU (72 KB of LDS each),
+//   and as they synchronise only internally, one workgroup's softmax runs
+//   while the other's MFMAs do.
+//   Per stage a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //   (A = K rows from LDS, B = the wave's Q rows, held in registers for the
 //   whole walk), so each lane holds 32 logits of ONE query row: the row max and
 //   row sum need one cross-lane step (lane l and l^32).  Then O^T += V^T P^T
@@ -25,24 +25,24 @@
 // half h hold keys 16c + 8h .. 16c + 8h + 7, which is exactly the B-operand
 // layout of a 16-key P chunk; the V^T operand reads the same keys.
 //
-// Data movement (double-buffered, one barrier per block)
-//   K and V of the next block are loaded into registers at the top of an
-//   iteration and written to the other LDS buffer after the current block's
-//   softmax, so the loads overlap the current block's MFMA and softmax work.
-//   (Direct global->LDS loads were tried: the compiler cannot prove that the
-//   DMA into one buffer does not alias reads of the other and waits for the
-//   loads before every LDS read, exposing the full memory latency.)
-//   K rows are 256 bytes whose 16-byte chunks are XOR-swizzled by the row
-//   number, so the 16 lanes that read one MFMA operand hit distinct banks;
-//   V is stored transposed (channel-major, rows padded to 272 bytes).
+// Data movement (double-buffered, one barrier per stage)
+//   K and V of the next stage are loaded into registers at the top of a stage
+//   and written to the other LDS buffer after the current stage's softmax, so
+//   the loads overlap the current stage's MFMA and softmax work.  (Direct
+//   global->LDS loads were tried: the compiler cannot prove that the DMA into
+//   one buffer does not alias reads of the other, and waits for the loads
+//   before every LDS read.)  K rows are 256 bytes whose 16-byte chunks are
+//   XOR-swizzled by the row number, so the 16 lanes reading one MFMA operand
+//   hit distinct banks; V is stored transposed, channel-major, in rows padded
+//   to 144 bytes (again conflict-free for the operand reads).
 //
 // Softmax: log2 domain with the scale folded in; the running max is only
-// raised when a block's max exceeds it by more than 8 (a factor 256), so the
-// O rescale is usually skipped; O/l and LSE = m + log2(l) are unchanged by the
+// raised when a stage's max exceeds it by more than 8 (a factor 256), so the
+// O rescale is usually skipped; O/l and LSE = m + log2(l) do not depend on the
 // choice of m.
 //
 // Workgroup numbering: dispatch hands workgroups to the 8 XCDs round-robin.
-// Tiles are numbered so that in every round of 8 x 32 resident workgroups all
+// Tiles are numbered so that in every round of 8 x 64 resident workgroups all
 // XCDs work on one contiguous run of tiles (the same head), each XCD on its
 // own contiguous sub-run: the head's K/V stays in the shared last-level cache
 // and neighbouring query tiles, whose kept blocks overlap, share an L2.
@@ -54,13 +54,14 @@ namespace {
 constexpr int D = 128;
 constexpr int BQ = 128;
 constexpr int BK = 128;
-constexpr int NT = 512;                       // threads per workgroup (8 waves)
-constexpr int KBUF = BK * D * 2;              // 32 KB, swizzled rows of 256 B
-constexpr int VSTR = BK * 2 + 16;             // bytes per V^T row (one channel)
-constexpr int VBUF = D * VSTR;                // 34 KB
-constexpr int MAX_KEPT = 4096;                // list entries staged in LDS
+constexpr int SK = 64;                        // keys per stage
+constexpr int NT = 256;                       // threads per workgroup (4 waves)
+constexpr int KBUF = SK * D * 2;              // 16 KB, swizzled rows of 256 B
+constexpr int VSTR = SK * 2 + 16;             // bytes per V^T row (one channel)
+constexpr int VBUF = D * VSTR;                // 18 KB
+constexpr int MAX_KEPT = 1024;                // list slots staged in LDS (the last holds the count)
 constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF + MAX_KEPT * 4;
-constexpr int RESIDENT_PER_XCD = 32;          // one workgroup per CU, 32 CUs per XCD
+constexpr int RESIDENT_PER_XCD = 64;          // two workgroups per CU, 32 CUs per XCD
 constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
 
 struct MfmaArgs {
@@ -88,58 +89,43 @@ __device__ __forceinline__ int64_t tile_of(int64_t w, int64_t tiles) {
   return r * round_sz + xcd * RESIDENT_PER_XCD + s;
 }
 
-struct KRegs {
-  uint4 r0, r1, r2, r3;
+struct Stage {
+  uint4 k0, k1, k2, k3;  // K: 16-byte chunks tid + 256 i of the 64 x 256-byte stage
+  uint4 v0, v1, v2, v3;  // V: keys 4*(tid%16) .. +3, channels 8*(tid/16) .. +7
 };
 
-// K block -> registers: thread t loads 16-byte chunks t, t+512, t+1024, t+1536
-// (row = chunk/16, logical chunk = chunk%16).
-__device__ __forceinline__ KRegs load_k(const uint16_t* kg, int tid) {
-  const uint16_t* p = kg + (tid >> 4) * D + (tid & 15) * 8;
-  KRegs k;
-  k.r0 = *reinterpret_cast<const uint4*>(p);
-  k.r1 = *reinterpret_cast<const uint4*>(p + 32 * D);
-  k.r2 = *reinterpret_cast<const uint4*>(p + 64 * D);
-  k.r3 = *reinterpret_cast<const uint4*>(p + 96 * D);
-  return k;
+__device__ __forceinline__ Stage load_stage(const uint16_t* kg, const uint16_t* vg, int tid) {
+  Stage s;
+  const uint16_t* kp = kg + (tid >> 4) * D + (tid & 15) * 8;
+  s.k0 = *reinterpret_cast<const uint4*>(kp);
+  s.k1 = *reinterpret_cast<const uint4*>(kp + 16 * D);
+  s.k2 = *reinterpret_cast<const uint4*>(kp + 32 * D);
+  s.k3 = *reinterpret_cast<const uint4*>(kp + 48 * D);
+  const uint16_t* vp = vg + (4 * (tid & 15)) * D + (tid >> 4) * 8;
+  s.v0 = *reinterpret_cast<const uint4*>(vp);
+  s.v1 = *reinterpret_cast<const uint4*>(vp + D);
+  s.v2 = *reinterpret_cast<const uint4*>(vp + 2 * D);
+  s.v3 = *reinterpret_cast<const uint4*>(vp + 3 * D);
+  return s;
 }
 
-// registers -> swizzled K rows: logical chunk c of row r sits at physical chunk c ^ (r & 15)
-__device__ __forceinline__ void store_k(uint8_t* kbuf, const KRegs& k, int tid) {
+__device__ __forceinline__ void store_stage(uint8_t* kbuf, uint8_t* vbuf, const Stage& s, int tid) {
+  // K: logical chunk c of row r sits at physical chunk c ^ (r & 15); rows r + 16 i share r & 15
   const int r = tid >> 4, c = tid & 15;
-  const int off = r * 256 + ((c ^ (r & 15)) * 16);  // rows r+32i keep the same r & 15
-  *reinterpret_cast<uint4*>(kbuf + off) = k.r0;
-  *reinterpret_cast<uint4*>(kbuf + off + 32 * 256) = k.r1;
-  *reinterpret_cast<uint4*>(kbuf + off + 64 * 256) = k.r2;
-  *reinterpret_cast<uint4*>(kbuf + off + 96 * 256) = k.r3;
-}
-
-struct VRegs {
-  uint4 r0, r1, r2, r3;
-};
-
-// V block -> registers: thread t loads keys 4*(t%32) .. +3, channels 8*(t/32) .. +7.
-__device__ __forceinline__ VRegs load_v(const uint16_t* vg, int tid) {
-  const int kgrp = tid & 31, dg = tid >> 5;
-  const uint16_t* p = vg + (4 * kgrp) * D + dg * 8;
-  VRegs v;
-  v.r0 = *reinterpret_cast<const uint4*>(p);
-  v.r1 = *reinterpret_cast<const uint4*>(p + D);
-  v.r2 = *reinterpret_cast<const uint4*>(p + 2 * D);
-  v.r3 = *reinterpret_cast<const uint4*>(p + 3 * D);
-  return v;
-}
-
-__device__ __forceinline__ void store_vt(uint8_t* vbuf, const VRegs& v, int tid) {
-  const int kgrp = tid & 31, dg = tid >> 5;
-  const uint32_t w0[4] = {v.r0.x, v.r0.y, v.r0.z, v.r0.w};
-  const uint32_t w1[4] = {v.r1.x, v.r1.y, v.r1.z, v.r1.w};
-  const uint32_t w2[4] = {v.r2.x, v.r2.y, v.r2.z, v.r2.w};
-  const uint32_t w3[4] = {v.r3.x, v.r3.y, v.r3.z, v.r3.w};
+  const int off = r * 256 + ((c ^ (r & 15)) * 16);
+  *reinterpret_cast<uint4*>(kbuf + off) = s.k0;
+  *reinterpret_cast<uint4*>(kbuf + off + 16 * 256) = s.k1;
+  *reinterpret_cast<uint4*>(kbuf + off + 32 * 256) = s.k2;
+  *reinterpret_cast<uint4*>(kbuf + off + 48 * 256) = s.k3;
+  // V^T: channel 8*dg + 2j from the low halves, 8*dg + 2j + 1 from the high halves.
+  // v_perm_b32 selects bytes of {a:b}: 0x05040100 = low halves (b, a), 0x07060302 = high halves.
+  const int kgrp = tid & 15, dg = tid >> 4;
+  const uint32_t w0[4] = {s.v0.x, s.v0.y, s.v0.z, s.v0.w};
+  const uint32_t w1[4] = {s.v1.x, s.v1.y, s.v1.z, s.v1.w};
+  const uint32_t w2[4] = {s.v2.x, s.v2.y, s.v2.z, s.v2.w};
+  const uint32_t w3[4] = {s.v3.x, s.v3.y, s.v3.z, s.v3.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // channel 8*dg + 2j from the low halves, 8*dg + 2j + 1 from the high halves
-    // v_perm_b32 selects bytes of {a:b}: 0x05040100 = low halves (b, a), 0x07060302 = high halves
     uint2 lo, hv;
     lo.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
     lo.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
@@ -151,9 +137,10 @@ __device__ __forceinline__ void store_vt(uint8_t* vbuf, const VRegs& v, int tid)
 }
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // buffer i of K at smem + i*KBUF, of V^T at smem + 2*KBUF + i*VBUF
+  // K buffer i at smem + i*KBUF, V^T buffer i at smem + 2*KBUF + i*VBUF, list after them
+  int32_t* lst = reinterpret_cast<int32_t*>(smem + 2 * KBUF + 2 * VBUF);
 
   const int64_t tile = tile_of(blockIdx.x, a.tiles);
   const int64_t t = tile % a.lists;
@@ -165,20 +152,37 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rw = wave & 3;     // row group: query rows 32*rw .. +31
-  const int half = wave >> 2;  // key half: keys 64*half .. +63 of each block
   const int li = lane & 31;
   const int hi = lane >> 5;
 
-  const int64_t qrow = t * BQ + rw * 32 + li;
+  const int64_t qrow = t * BQ + wave * 32 + li;
   const uint16_t* qp = a.q + ((b * a.heads_q + h) * a.len_q + qrow) * D;
   bf16x8 qf[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hi);
-  // settle the Q loads here (a compiler-visible vmcnt(0)): otherwise the
-  // wait-count bookkeeping at the loop head cannot tell them from the in-loop
-  // prefetches and makes every block wait for the next block's loads
+
+  // compact the tile's list into LDS (valid blocks only, order kept): wave 0, 64 entries a step
+  const int nblk_k = (int)(a.len_k / BK);
+  if (wave == 0) {
+    const int32_t* g = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int n = 0;
+    for (int base = 0; base < a.kept; base += 64) {
+      const int e = base + lane;
+      const int32_t blk = e < a.kept ? g[e] : -1;
+      const bool ok = blk >= 0 && blk < nblk_k;
+      const uint64_t m = __ballot(ok);
+      if (ok) lst[n + __popcll(m & below)] = blk;
+      n += __popcll(m);
+    }
+    if (lane == 0) lst[MAX_KEPT - 1] = n;  // kept < MAX_KEPT, so the count slot is never an entry
+  }
+  // settle the Q loads with a compiler-visible vmcnt(0): otherwise the wait-count
+  // bookkeeping at the loop head cannot tell them from the in-loop prefetches
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  const int n_valid = lst[MAX_KEPT - 1];
+  const int n_stage = 2 * n_valid;
 
   f32x16 oacc[4];
 #pragma unroll
@@ -188,58 +192,35 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
   float m = -INFINITY;  // running row max of scale*log2(e)*logit (lazily raised)
   float l = 0.f;        // this lane's share of the running row sum
 
-  // the tile's key list, staged in LDS once (after the K/V buffers)
-  int32_t* lst = reinterpret_cast<int32_t*>(smem + 2 * KBUF + 2 * VBUF);
-  {
-    const int32_t* g = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
-    for (int i = tid; i < a.kept; i += NT) lst[i] = g[i];
-  }
-  __syncthreads();
   const uint16_t* kbase = a.k + (b * a.heads_kv + hk) * a.len_k * D;
   const uint16_t* vbase = a.v + (b * a.heads_kv + hk) * a.len_k * D;
   const int krow_l = swap_bits_2_3(li);
-  const int nblk_k = (int)(a.len_k / BK);
 
-  // find the first valid entry (empty or out-of-range slots are skipped)
-  int e = 0;
-  int blk = -1;
-  for (; e < a.kept; ++e) {
-    blk = lst[e];
-    if (blk >= 0 && blk < nblk_k) break;
-  }
-  int buf = 0;
-  if (e < a.kept) {
-    const KRegs k0 = load_k(kbase + (int64_t)blk * BK * D, tid);
-    const VRegs v0 = load_v(vbase + (int64_t)blk * BK * D, tid);
-    store_k(smem, k0, tid);
-    store_vt(smem + 2 * KBUF, v0, tid);
+  if (n_stage > 0) {
+    const int64_t off = (int64_t)lst[0] * BK * D;
+    const Stage s0 = load_stage(kbase + off, vbase + off, tid);
+    store_stage(smem, smem + 2 * KBUF, s0, tid);
   }
   __syncthreads();
 
-  while (e < a.kept) {
-    // next valid entry
-    int e_next = e + 1;
-    int blk_next = -1;
-    for (; e_next < a.kept; ++e_next) {
-      blk_next = lst[e_next];
-      if (blk_next >= 0 && blk_next < nblk_k) break;
-    }
-    const bool has_next = e_next < a.kept;
-    KRegs kn;
-    VRegs vn;
+  for (int st_i = 0; st_i < n_stage; ++st_i) {
+    const int buf = st_i & 1;
+    const bool has_next = st_i + 1 < n_stage;
+    Stage nx;
     if (has_next) {
-      kn = load_k(kbase + (int64_t)blk_next * BK * D, tid);
-      vn = load_v(vbase + (int64_t)blk_next * BK * D, tid);
+      const int sn = st_i + 1;
+      const int64_t off = (int64_t)lst[sn >> 1] * BK * D + (int64_t)(sn & 1) * SK * D;
+      nx = load_stage(kbase + off, vbase + off, tid);
     }
 
-    // S^T = K Q^T for this wave's two 32-key sub-tiles
+    // S^T = K Q^T for the stage's two 32-key sub-tiles
     const uint8_t* kcur = smem + buf * KBUF;
     f32x16 s[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
-      const int krow = 64 * half + 32 * st + krow_l;
+      const int krow = 32 * st + krow_l;
       const uint8_t* rowp = kcur + krow * 256;
       bf16x8 af[8];
 #pragma unroll
@@ -279,12 +260,10 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
       }
     l += psum;
 
-    if (has_next) {  // the next block's buffers were last read before the previous barrier
-      store_k(smem + (buf ^ 1) * KBUF, kn, tid);
-      store_vt(smem + 2 * KBUF + (buf ^ 1) * VBUF, vn, tid);
-    }
+    if (has_next)  // the other buffers were last read before the previous barrier
+      store_stage(smem + (buf ^ 1) * KBUF, smem + 2 * KBUF + (buf ^ 1) * VBUF, nx, tid);
 
-    // O^T += V^T P^T over this wave's 64 keys, 16 at a time
+    // O^T += V^T P^T over the stage's 64 keys, 16 at a time
     const uint8_t* vcur = smem + 2 * KBUF + buf * VBUF;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -293,7 +272,7 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
         bf16x8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[st][8 * cc + j];
-        const int key0 = 64 * half + 32 * st + 16 * cc + 8 * hi;
+        const int key0 = 32 * st + 16 * cc + 8 * hi;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vcur + (32 * u + li) * VSTR + 2 * key0);
@@ -302,32 +281,10 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
       }
     }
     __syncthreads();  // the current buffers are free; the next ones are complete
-    buf ^= 1;
-    e = e_next;
-    blk = blk_next;
   }
 
-  // merge the two key halves: waves 4-7 hand (m, l, O) to waves 0-3 through LDS
-  float* xo = reinterpret_cast<float*>(smem);                     // [4 waves][64 regs][64 lanes]
-  float* xm = reinterpret_cast<float*>(smem + 4 * 64 * 64 * 4);  // [4 waves][64 lanes]
-  float* xl = xm + 4 * 64;
-  if (half == 1) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(rw * 64 + u * 16 + r) * 64 + lane] = oacc[u][r];
-    xm[rw * 64 + lane] = m;
-    xl[rw * 64 + lane] = l;
-  }
-  __syncthreads();
-  if (half == 1) return;
-  const float m2 = xm[rw * 64 + lane];
-  const float l2 = xl[rw * 64 + lane];
-  const float mm = fmaxf(m, m2);
-  const float f1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
-  const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
-  const float lane_l = l * f1 + l2 * f2;
-  const float l_tot = lane_l + __shfl_xor(lane_l, 32);
+  // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
+  const float l_tot = l + __shfl_xor(l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t orow = (b * a.heads_q + h) * a.len_q + qrow;
 #pragma unroll
@@ -335,35 +292,30 @@ __global__ __launch_bounds__(NT, 1) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int ch = 32 * u + 8 * rq + 4 * hi;
-      float vv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * rq + j;
-        vv[j] = (oacc[u][r] * f1 + xo[(rw * 64 + u * 16 + r) * 64 + lane] * f2) * inv;
-      }
+      const float v0 = oacc[u][4 * rq + 0] * inv, v1 = oacc[u][4 * rq + 1] * inv;
+      const float v2 = oacc[u][4 * rq + 2] * inv, v3 = oacc[u][4 * rq + 3] * inv;
       if constexpr (OUT_BF16) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(vv[0]) | ((uint32_t)f32_to_bf16_bits(vv[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(vv[2]) | ((uint32_t)f32_to_bf16_bits(vv[3]) << 16);
+        pk.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + orow * D + ch) = pk;
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow * D + ch) =
-            make_float4(vv[0], vv[1], vv[2], vv[3]);
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow * D + ch) = make_float4(v0, v1, v2, v3);
       }
     }
   }
-  if (hi == 0) a.lse[orow] = l_tot > 0.f ? (mm + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (hi == 0) a.lse[orow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
 bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype) {
   const basa_kv_segment& g = d->seg[0];
+  // the list is compacted into the first MAX_KEPT-1 LDS slots; the last holds the count
   return q_dtype == BASA_BF16 && d->n_segments == 1 && g.dtype == BASA_BF16 && g.shift == 0 &&
          g.bias == 0.f && d->head_dim == D && d->tile_q == BQ && d->block_k == BK &&
          d->q_rows == nullptr && d->lists * BQ == d->len_q && d->scale > 0.0 &&
-         g.count <= MAX_KEPT &&
-         (o_dtype == BASA_BF16 || o_dtype == BASA_F32);
+         g.count < MAX_KEPT && (o_dtype == BASA_BF16 || o_dtype == BASA_F32);
 }
 
 hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int o_dtype,
