@@ -89,6 +89,53 @@ def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
                       f"{w.heads} heads (est. {est:.0f} s for the whole step)"}
 
 
+def _time(torch, fn, reps=10):
+    """Average wall time of fn() over reps calls, bracketed by HIP events on the launch stream."""
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def llsa_and_losa_stages(torch, wl, basa) -> dict:
+    """The hierarchical (log-linear) forward on the 256x256-image workload and the
+    LoSA prefix step on the 64K-prefix workload."""
+    import math
+    import block_sparse_attention_mean_amd.pipelines as pl
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    out = {}
+    x = wl.generate("llsa64k")
+    f = pl.LlsaForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), 16, 8, 1.0 / 8)
+    t_pool, t_sel, t_attn = _time(torch, f.pool), _time(torch, f.select), _time(torch, f.attend)
+    n, h, d = 65536, 4, 64
+    keys = 400
+    flops = 4.0 * h * n * keys * d
+    out["llsa64k"] = {"ms": t_pool + t_sel + t_attn, "pool_ms": t_pool, "select_ms": t_sel,
+                      "attn_ms": t_attn, "attn_TFLOP/s": flops / (t_attn * 1e-3) / 1e12,
+                      "keys_per_query": keys}
+    y = wl.make_losa(1004)
+    hq, t, dd = 32, 16, 128
+    cache_o = torch.zeros(1, hq, t, dd, dtype=torch.float32, device="cuda")
+    cache_lse = torch.zeros(1, hq, t, dtype=torch.float32, device="cuda")
+    s = pl.LosaStep(dev(y["q_cur"]), dev(y["q_prev"]), dev(y["k_prefix"]), dev(y["v_prefix"]),
+                    dev(y["k_block"]), dev(y["v_block"]), cache_o, cache_lse, 5, 16, 128,
+                    1.0 / math.sqrt(128))
+    t_prep = _time(torch, s.prepare)
+    t_step = _time(torch, s.step)
+    out["losa64k_step"] = {"ms": t_step, "prefix_pool_ms": t_prep,
+                           "note": "per denoising step: active-token pick, selection, sparse prefix "
+                                   "attention for 5 tokens x 32 heads, in-block attention, merge"}
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -205,6 +252,7 @@ def main():
                            "frac_hbm": merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "max_abs_vs_one_shot": float((om.float() - o.float()).abs().max())}
         del oa, ob, la, lb, om, lm
+        stages.update(llsa_and_losa_stages(torch, wl, basa))
 
     result = {
         "metric": "block-sparse attn TFLOP/s (kept blocks) + % MFMA peak at L=64K, d=128",

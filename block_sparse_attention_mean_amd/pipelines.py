@@ -1,0 +1,210 @@
+"""The three workflows of the method as sequences of libbasa calls.
+
+Every arithmetic step runs in the HIP kernels; this module only allocates
+intermediate device buffers (torch) and chains the four C calls.
+
+* ba_forward       - BA-Att paper, section 3.1 / Algorithm 1 without sorting
+                     or compensation: pool Q and K per block, score the blocks,
+                     keep the top-k key blocks per query block, attend.
+* llsa_forward     - log-linear sparse attention (loglinear-sparse-dit
+                     README): levels of 16-token means, coarse-to-fine per-token
+                     top-k, attention over fine survivors plus every coarse
+                     candidate with a level bias l*ln(block).
+* losa_step        - LoSA post: active tokens by query change, sparse prefix
+                     attention for active rows written into the cached
+                     (O, LSE), dense in-block attention, online-softmax merge.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (SELECT_BLOCKS, SELECT_CHANGE, basa_attn, basa_merge, basa_pool, basa_select,
+               kv_segment)
+
+
+def _empty(*shape, dtype, like):
+    return torch.empty(*shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+# BA-Att selection + block-sparse attention
+# ---------------------------------------------------------------------------
+
+class BaForward:
+    """Buffers and calls of one BA-Att forward for fixed shapes.
+
+    q, k, v [B, H, L, d] bf16 (or float32); block = query/key block size;
+    topk = kept key blocks per query block.  run() fills self.idx (int32
+    [B, H, L/block, topk], ascending), self.o and self.lse.
+    """
+
+    def __init__(self, q, k, v, block: int, topk: int, scale: float | None = None,
+                 o_dtype=None):
+        b, h, length, d = q.shape
+        self.q, self.k, self.v = q, k, v
+        self.block, self.topk = block, topk
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        nb = length // block
+        self.qbar = _empty(b, h, nb, d, dtype=torch.float64, like=q)
+        self.kbt = _empty(b, k.shape[1], d, k.shape[2] // block, dtype=torch.float64, like=q)
+        self.idx = _empty(b, h, nb, topk, dtype=torch.int32, like=q)
+        self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
+        self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
+
+    def select(self):
+        basa_pool(self.q, self.block, mean_rows=self.qbar)
+        basa_pool(self.k, self.block, mean_cols=self.kbt)
+        basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=self.scale)
+
+    def attend(self):
+        basa_attn(self.q, kv_segment(self.idx, self.k, self.v), self.o, self.lse,
+                  tile_q=self.block, block_k=self.block, scale=self.scale)
+
+    def run(self):
+        self.select()
+        self.attend()
+        return self.o, self.lse
+
+
+def ba_forward(q, k, v, block: int, topk: int, scale: float | None = None):
+    f = BaForward(q, k, v, block, topk, scale)
+    f.run()
+    return f.idx, f.o, f.lse
+
+
+# ---------------------------------------------------------------------------
+# Log-linear hierarchical top-k
+# ---------------------------------------------------------------------------
+
+def llsa_levels(n: int, block: int) -> int:
+    """Coarse levels used for n tokens: the largest L with block^(L+1) | n."""
+    if n % block:
+        raise ValueError(f"{n} tokens is not a multiple of block {block}")
+    lv = 0
+    while n % (block ** (lv + 2)) == 0:
+        lv += 1
+    return lv
+
+
+class LlsaForward:
+    """Buffers and calls of one log-linear sparse attention forward.
+
+    q, k, v [B, H, N, d] bf16; block (pooling factor and fine key block),
+    topk per query token.  At most three coarse levels (four key segments).
+    run() fills self.sel[l] for l = 1..L (int32 [B, H, N/block^l, topk]),
+    self.o and self.lse.
+    """
+
+    def __init__(self, q, k, v, block: int = 16, topk: int = 8, scale: float | None = None):
+        b, h, n, d = q.shape
+        self.q, self.k, self.v = q, k, v
+        self.block, self.topk = block, topk
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.levels = llsa_levels(n, block)
+        if not 1 <= self.levels <= 3:
+            raise ValueError(f"{self.levels} coarse levels: this path supports 1 to 3")
+        f64, f32 = torch.float64, torch.float32
+        self.qm, self.km, self.kt, self.vm, self.kf, self.vf, self.sel = {}, {}, {}, {}, {}, {}, {}
+        for lv in range(1, self.levels + 1):
+            nl = n // block ** lv
+            self.qm[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
+            self.km[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
+            self.kt[lv] = _empty(b, h, d, nl, dtype=f64, like=q)
+            self.vm[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
+            self.kf[lv] = _empty(b, h, nl, d, dtype=f32, like=q)
+            self.vf[lv] = _empty(b, h, nl, d, dtype=f32, like=q)
+            self.sel[lv] = _empty(b, h, nl, topk, dtype=torch.int32, like=q)
+        # every token of the top level is a candidate: all of its 16-token blocks
+        n_top_blocks = (n // block ** self.levels) // block
+        self.top_all = torch.arange(n_top_blocks, dtype=torch.int32, device=q.device).expand(
+            b, h, 1, n_top_blocks).contiguous()
+        self.o = torch.empty_like(q)
+        self.lse = _empty(b, h, n, dtype=f32, like=q)
+
+    def pool(self):
+        bl = self.block
+        for lv in range(1, self.levels + 1):
+            sq = self.q if lv == 1 else self.qm[lv - 1]
+            sk = self.k if lv == 1 else self.km[lv - 1]
+            sv = self.v if lv == 1 else self.vm[lv - 1]
+            basa_pool(sq, bl, mean_rows=self.qm[lv])
+            basa_pool(sk, bl, mean_rows=self.km[lv], mean_cols=self.kt[lv], mean_copy=self.kf[lv])
+            basa_pool(sv, bl, mean_rows=self.vm[lv], mean_copy=self.vf[lv])
+
+    def select(self):
+        top = self.levels
+        basa_select(self.qm[top], self.kt[top], self.sel[top], self.topk, scale=self.scale)
+        for lv in range(top - 1, 0, -1):
+            basa_select(self.qm[lv], self.kt[lv], self.sel[lv], self.topk, scale=self.scale,
+                        parent=self.sel[lv + 1], fanout=self.block)
+
+    def attend(self):
+        bl, lb = self.block, math.log(self.block)
+        segs = [kv_segment(self.sel[1], self.k, self.v)]          # fine keys: children of level-1 picks
+        for lv in range(1, self.levels):                          # level-lv candidates
+            segs.append(kv_segment(self.sel[lv + 1], self.kf[lv], self.vf[lv],
+                                   shift=4 * lv, bias=lv * lb))
+        top = self.levels                                          # every top-level token
+        segs.append(kv_segment(self.top_all, self.kf[top], self.vf[top], shift=30,
+                               bias=top * lb))
+        basa_attn(self.q, segs, self.o, self.lse, tile_q=bl, block_k=bl, scale=self.scale)
+
+    def run(self):
+        self.pool()
+        self.select()
+        self.attend()
+        return self.o, self.lse
+
+
+# ---------------------------------------------------------------------------
+# LoSA denoising step
+# ---------------------------------------------------------------------------
+
+class LosaStep:
+    """Buffers and calls of one LoSA denoising step of a block.
+
+    q_cur, q_prev [B, Hq, T, d] bf16; k_prefix, v_prefix [B, Hkv, P, d] bf16;
+    k_block, v_block [B, Hkv, T, d]; cache_o [B, Hq, T, d] float32 and
+    cache_lse [B, Hq, T] float32 are updated in place for the active rows.
+    prepare() pools the prefix keys (once per generation block); step() runs
+    the per-step work and fills self.active, self.sel, self.o (bf16), self.lse.
+    """
+
+    def __init__(self, q_cur, q_prev, k_prefix, v_prefix, k_block, v_block, cache_o, cache_lse,
+                 n_active: int = 5, block: int = 16, topk: int = 128, scale: float | None = None):
+        b, hq, t, d = q_cur.shape
+        self.q_cur, self.q_prev = q_cur, q_prev
+        self.k_prefix, self.v_prefix = k_prefix, v_prefix
+        self.k_block, self.v_block = k_block, v_block
+        self.cache_o, self.cache_lse = cache_o, cache_lse
+        self.n_active, self.block, self.topk = n_active, block, topk
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        hkv, p = k_prefix.shape[1], k_prefix.shape[2]
+        self.active = _empty(b, n_active, dtype=torch.int32, like=q_cur)
+        self.q64 = _empty(b, hq, t, d, dtype=torch.float64, like=q_cur)
+        self.kbt = _empty(b, hkv, d, p // block, dtype=torch.float64, like=q_cur)
+        self.sel = _empty(b, hq, n_active, topk, dtype=torch.int32, like=q_cur)
+        self.inblock = torch.zeros(b, hq, 1, 1, dtype=torch.int32, device=q_cur.device)
+        self.o_in = _empty(b, hq, t, d, dtype=torch.float32, like=q_cur)
+        self.lse_in = _empty(b, hq, t, dtype=torch.float32, like=q_cur)
+        self.o = torch.empty_like(q_cur)
+        self.lse = _empty(b, hq, t, dtype=torch.float32, like=q_cur)
+
+    def prepare(self):
+        basa_pool(self.k_prefix, self.block, mean_cols=self.kbt)
+
+    def step(self):
+        t = self.q_cur.shape[2]
+        basa_select(self.q_cur, self.q_prev, self.active, self.n_active, mode=SELECT_CHANGE)
+        basa_pool(self.q_cur, 1, mean_rows=self.q64)
+        basa_select(self.q64, self.kbt, self.sel, self.topk, scale=self.scale,
+                    q_rows=self.active)
+        basa_attn(self.q_cur, kv_segment(self.sel, self.k_prefix, self.v_prefix), self.cache_o,
+                  self.cache_lse, tile_q=1, block_k=self.block, scale=self.scale,
+                  q_rows=self.active)
+        basa_attn(self.q_cur, kv_segment(self.inblock, self.k_block, self.v_block), self.o_in,
+                  self.lse_in, tile_q=t, block_k=t, scale=self.scale)
+        basa_merge(self.cache_o, self.cache_lse, self.o_in, self.lse_in, self.o, self.lse)
+        return self.o, self.lse

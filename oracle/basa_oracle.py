@@ -155,20 +155,25 @@ def sparse_attention(q, k, v, kv_idx, tile_q: int, block_k: int, scale: float,
 def dense_attention(q, k, v, scale: float):
     """Full softmax attention (BA-Att section 2, Eq. 1), bidirectional.
 
-    q [B, Hq, Lq, d], k/v [B, Hkv, Lk, d]; returns O and natural-log LSE.
+    q [B, Hq, Lq, d], k/v [B, Hkv, Lk, d] (query head h reads key head
+    h // (Hq/Hkv)); returns O and natural-log LSE.
     """
     q = as_f64(q)
-    k = as_f64(k)
-    v = as_f64(v)
-    group = q.shape[1] // k.shape[1]
-    if group > 1:
-        k = np.repeat(k, group, axis=1)
-        v = np.repeat(v, group, axis=1)
-    z = scale * np.matmul(q, np.swapaxes(k, -1, -2))
-    m = z.max(axis=-1, keepdims=True)
-    e = np.exp(z - m)
-    s = e.sum(axis=-1, keepdims=True)
-    return np.matmul(e, v) / s, (m + np.log(s))[..., 0]
+    nb, hq = q.shape[:2]
+    group = hq // np.asarray(k).shape[1]
+    o = np.empty(q.shape[:3] + (np.asarray(v).shape[-1],))
+    lse = np.empty(q.shape[:3])
+    for b in range(nb):
+        for hk in range(np.asarray(k).shape[1]):
+            kh, vh = as_f64(k[b, hk]), as_f64(v[b, hk])
+            for h in range(hk * group, (hk + 1) * group):
+                z = scale * (q[b, h] @ kh.T)
+                m = z.max(axis=-1, keepdims=True)
+                e = np.exp(z - m)
+                s = e.sum(axis=-1, keepdims=True)
+                o[b, h] = (e @ vh) / s
+                lse[b, h] = (m + np.log(s))[:, 0]
+    return o, lse
 
 
 def merge(o_a, lse_a, o_b, lse_b):
@@ -349,8 +354,9 @@ def losa_step(q_cur, q_prev, k_prefix, v_prefix, k_block, v_block, cache_o, cach
     new_lse = np.asarray(cache_lse, dtype=np.float64).copy()
     for b in range(nb):
         for h in range(hq):
-            kh = as_f64(k_prefix[b, h // group])
-            vh = as_f64(v_prefix[b, h // group])
+            if h % group == 0:
+                kh = as_f64(k_prefix[b, h // group])
+                vh = as_f64(v_prefix[b, h // group])
             for j, t in enumerate(act[b]):
                 scores = scale * (kbar[b, h // group] @ qc[b, h, t])
                 sel[b, h, j] = topk_ascending(scores, topk)

@@ -1,0 +1,96 @@
+"""Whole workflows through the C ABI against the fp64 oracle, at full size.
+
+* BA-Att forward on the 64K-token workload: every selected index bit-exact,
+  attention on sampled query tiles (the oracle computes them one by one).
+* Log-linear hierarchical top-k on the 256 x 256 image workload: every level's
+  selection bit-exact, O and LSE on all rows.
+* LoSA prefix step on the 64K-prefix workload: active tokens and selections
+  bit-exact, O / LSE / updated cache rows on all rows.
+Tolerances: O 2e-2, LSE 1e-3 (bf16 inputs, float32 accumulation).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from gpu_util import LSE_TOL, O_TOL, dev, host, max_err, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pipes():
+    assert torch.cuda.is_available(), "the GPU tests need a visible GPU"
+    import block_sparse_attention_mean_amd.pipelines as p
+    return p
+
+
+def test_ba_forward_dlm64k_indices_full_and_sampled_tiles(pipes):
+    note("BA-Att forward dlm64k: H32 L65536 block128 top128")
+    w = wl.WORKLOADS["dlm64k"]
+    x = wl.generate("dlm64k")
+    f = pipes.BaForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.block, w.topk)
+    f.run()
+    torch.cuda.synchronize()
+    ref_idx = orc.topk_ascending(orc.block_logits(orc.pool_mean(x["q"], w.block),
+                                                  orc.pool_mean(x["k"], w.block), w.scale), w.topk)
+    assert np.array_equal(host(f.idx), ref_idx)
+    g = np.random.Generator(np.random.PCG64(31))
+    lists = [(0, int(h), int(t)) for h, t in zip(g.integers(0, w.heads, 24), g.integers(0, w.blocks, 24))]
+    lists += [(0, 0, 0), (0, w.heads - 1, w.blocks - 1)]
+    o, lse = host(f.o), host(f.lse)
+    for b, h, t in lists:
+        rows = slice(t * w.block, (t + 1) * w.block)
+        ro, rl = orc.attend_rows(x["q"][b, h, rows], x["k"][b, h], x["v"][b, h], ref_idx[b, h, t],
+                                 w.block, w.scale)
+        assert max_err(o[b, h, rows], ro) <= O_TOL, (h, t)
+        assert max_err(lse[b, h, rows], rl) <= LSE_TOL, (h, t)
+
+
+@pytest.mark.parametrize("n,heads,d", [(1024, 2, 64), (4096, 3, 64), (65536, 4, 64)])
+def test_llsa_forward_matches_oracle(pipes, n, heads, d):
+    note(f"LLSA forward N{n} H{heads} d{d}")
+    if n == 65536:
+        x = wl.generate("llsa64k")
+    else:
+        g = np.random.Generator(np.random.PCG64(n))
+        x = {k: wl.f32_to_bf16(g.standard_normal((1, heads, n, d)).astype(np.float32)) for k in "qkv"}
+    scale = 1.0 / math.sqrt(d)
+    f = pipes.LlsaForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), 16, 8, scale)
+    f.run()
+    torch.cuda.synchronize()
+    ref = orc.llsa_forward(x["q"][0], x["k"][0], x["v"][0], 16, 8, scale)
+    assert ref["levels"] == f.levels
+    for lv in range(1, f.levels + 1):
+        assert np.array_equal(host(f.sel[lv])[0], ref["sel"][lv]), lv
+    assert max_err(host(f.o)[0], ref["o"]) <= O_TOL
+    assert max_err(host(f.lse)[0], ref["lse"]) <= LSE_TOL
+
+
+@pytest.mark.parametrize("prefix,topk", [(1024, 8), (65536, 128)])
+def test_losa_step_matches_oracle(pipes, prefix, topk):
+    note(f"LoSA step prefix {prefix} top-{topk}")
+    x = wl.make_losa(1004 if prefix == 65536 else 77, prefix=prefix)
+    scale = 1.0 / math.sqrt(128)
+    co, cl = orc.dense_attention(x["q_prev"], x["k_prefix"], x["v_prefix"], scale)
+    co32, cl32 = co.astype(np.float32), cl.astype(np.float32)
+    cache_o, cache_lse = dev(co32), dev(cl32)
+    s = pipes.LosaStep(dev(x["q_cur"]), dev(x["q_prev"]), dev(x["k_prefix"]), dev(x["v_prefix"]),
+                       dev(x["k_block"]), dev(x["v_block"]), cache_o, cache_lse, 5, 16, topk, scale)
+    s.prepare()
+    s.step()
+    torch.cuda.synchronize()
+    ref = orc.losa_step(x["q_cur"], x["q_prev"], x["k_prefix"], x["v_prefix"], x["k_block"],
+                        x["v_block"], co32, cl32, 5, 16, topk, scale)
+    assert np.array_equal(host(s.active), ref["active"])
+    assert host(s.active).tolist() == [list(wl.LOSA_PLANTED)]
+    assert np.array_equal(host(s.sel), ref["sel"])
+    assert max_err(host(cache_o), ref["cache_o"]) <= 1e-3
+    assert max_err(host(cache_lse), ref["cache_lse"]) <= LSE_TOL
+    assert max_err(host(s.o), ref["o"]) <= O_TOL
+    assert max_err(host(s.lse), ref["lse"]) <= LSE_TOL
+    stable = [t for t in range(16) if t not in wl.LOSA_PLANTED]
+    assert np.array_equal(host(cache_o)[:, :, stable], co32[:, :, stable].astype(np.float64))
