@@ -31,6 +31,12 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# HBM traffic of one attention-kernel launch on this workload, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (separate runs), each scaled by the same counter on a 1 GiB
+# device copy (factors 2.0 and 1.0); see profiles/attn_mfma_dlm64k.md.  Valid only for
+# the kernel source it was measured on (first 16 hex digits of its sha256).
+MEASURED_ATTN_TRAFFIC = {"source_sha256": "b5d197ce078e12ca", "fetch_bytes": 64.070e9, "write_bytes": 0.545e9}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -54,6 +60,18 @@ def copy_probe(nbytes: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": 5}))
+
+
+def attn_traffic(workload: str):
+    """Counter-measured HBM bytes of one attention launch, or None when the kernel source
+    changed since the counters were taken (or for another workload)."""
+    import hashlib
+    src = os.path.join(ROOT, "block_sparse_attention_mean_amd", "csrc", "attn_mfma.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    m = MEASURED_ATTN_TRAFFIC
+    if workload != "dlm64k" or h != m["source_sha256"]:
+        return None
+    return m["fetch_bytes"] + m["write_bytes"]
 
 
 def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
@@ -271,7 +289,8 @@ def main():
                                f"block {w.block}, top-{w.topk} of {nb} key blocks, bidirectional",
                    "global_batch": 1, "seq_len": w.tokens, "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": attn_traffic(w.name)},
         "pct_mfma_peak_step": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "stages": stages,
     }
