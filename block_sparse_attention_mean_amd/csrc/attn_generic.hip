@@ -140,15 +140,16 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(GenArgs a) {
       m = m_new;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[i] *= alpha;
+      // empty slots carry p = 0 and a valid row of this head (some key of the chunk is valid)
       p_s[wave][lane] = p;
-      krow_s[wave][lane] = krow;
+      krow_s[wave][lane] = krow >= 0 ? krow : head_row;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int cnt = (int)((n_keys - k0) < 64 ? (n_keys - k0) : 64);
-      for (int j = 0; j < cnt; ++j) {
+      // fixed trip count and no data-dependent exits, so the V loads of several keys are in flight
+#pragma unroll 8
+      for (int j = 0; j < 64; ++j) {
         const float pj = p_s[wave][j];
-        if (pj == 0.f) continue;
         const int64_t kr = krow_s[wave][j];
 #pragma unroll
         for (int i = 0; i < CPL; ++i)

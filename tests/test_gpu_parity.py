@@ -247,31 +247,36 @@ def test_attn_generic_tiny_fp32(basa):
     assert max_err(lse, rl) <= 1e-5
 
 
-def test_attn_generic_segments_bias_and_f32_tables(basa):
-    note("attn generic: 3 segments (bf16 fine + f32 coarse, shifts, level bias), d64 tile16")
-    g = np.random.Generator(np.random.PCG64(24))
-    n, d, blk = 1024, 64, 16
+@pytest.mark.parametrize("tile_q", [16, 7, 32])
+def test_attn_segments_bias_and_f32_tables(basa, tile_q):
+    note(f"attn segments: bf16 fine + f32 coarse tables, shifts, level bias, d64 tile {tile_q}")
+    g = np.random.Generator(np.random.PCG64(24 + tile_q))
+    d, blk = 64, 16
+    tiles = 64
+    n = tile_q * tiles
+    n_keys = 1024
     q = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
-    kf = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
-    vf = wl.f32_to_bf16(g.standard_normal((1, 2, n, d)).astype(np.float32))
+    kf = wl.f32_to_bf16(g.standard_normal((1, 2, n_keys, d)).astype(np.float32))
+    vf = wl.f32_to_bf16(g.standard_normal((1, 2, n_keys, d)).astype(np.float32))
     k1 = g.standard_normal((1, 2, 64, d)).astype(np.float32)
     v1 = g.standard_normal((1, 2, 64, d)).astype(np.float32)
-    tiles = n // 16
-    i0 = np.sort(g.integers(0, n // blk, (1, 2, tiles, 8)), axis=-1).astype(np.int32)
+    i0 = np.sort(g.integers(0, n_keys // blk, (1, 2, tiles, 8)), axis=-1).astype(np.int32)
+    i0[0, 1, 5, 3] = -1                                   # an empty slot
     i1 = np.sort(g.integers(0, 64 // blk, (1, 2, tiles >> 4, 3)), axis=-1).astype(np.int32)
     i2 = np.zeros((1, 2, 1, 1), dtype=np.int32)
     b1, b2 = math.log(16), 2 * math.log(16)
     segs = [(i0, kf, vf, {}), (i1, k1, v1, {"shift": 4, "bias": b1}),
             (i2, k1, v1, {"shift": 10, "bias": b2})]
-    o, lse = run_attn(basa, q, segs, 16, blk, 0.125, torch.float32)
+    o, lse = run_attn(basa, q, segs, tile_q, blk, 0.125, torch.float32)
     # oracle: one table [fine | coarse] with per-entry bias
     kt = np.concatenate([orc.as_f64(kf), k1.astype(np.float64)], axis=2)
     vt = np.concatenate([orc.as_f64(vf), v1.astype(np.float64)], axis=2)
-    off = n // blk
-    full = np.concatenate([i0, np.repeat(i1, 16, axis=2) + off, np.repeat(i2, tiles, axis=2) + off], axis=-1)
+    off = n_keys // blk
+    full = np.concatenate([i0, np.where(np.repeat(i1, 16, axis=2) >= 0, np.repeat(i1, 16, axis=2) + off, -1),
+                           np.repeat(i2, tiles, axis=2) + off], axis=-1)
     bias = np.concatenate([np.zeros(i0.shape), np.full(i1.shape[:2] + (tiles, 3), b1),
                            np.full(i2.shape[:2] + (tiles, 1), b2)], axis=-1)
-    ro, rl = orc.sparse_attention(q, kt, vt, full, 16, blk, 0.125, bias=np.repeat(bias, 1, axis=2))
+    ro, rl = orc.sparse_attention(q, kt, vt, full, tile_q, blk, 0.125, bias=bias)
     assert max_err(o, ro) <= 1e-4
     assert max_err(lse, rl) <= 1e-4
 
