@@ -35,6 +35,54 @@ struct SelArgs {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// Wave-level top-k over KPL keys per lane in candidate order (lane + 64 j).
+// Marks sel[j] for the min(k, #valid) best under (key desc, candidate asc):
+// bitwise search from the top for the largest threshold T with at least k
+// keys >= T, stopping early when exactly k clear it; otherwise T is the k-th
+// largest key and keys equal to T are taken in candidate order.
+template <int KPL>
+__device__ __forceinline__ void wave_topk(const uint64_t* key, const bool* valid, int k,
+                                          uint64_t below, bool* sel) {
+  int n_valid = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) n_valid += popc64(__ballot(valid[j]));
+  if (n_valid <= k) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sel[j] = valid[j];
+    return;
+  }
+  uint64_t thr = 0;
+  bool exact = false;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t t = thr | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) cnt += popc64(__ballot(valid[j] && key[j] >= t));
+    if (cnt >= k) {
+      thr = t;
+      if (cnt == k) { exact = true; break; }
+    }
+  }
+  if (exact) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sel[j] = valid[j] && key[j] >= thr;
+    return;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gt += popc64(__ballot(valid[j] && key[j] > thr));
+  const int need_eq = k - gt;
+  int eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool eq = valid[j] && key[j] == thr;
+    const uint64_t em = __ballot(eq);
+    const int eq_rank = eq_seen + popc64(em & below);
+    eq_seen += popc64(em);
+    sel[j] = (valid[j] && key[j] > thr) || (eq && eq_rank < need_eq);
+  }
+}
+
 template <int KPL, int RW>
 __global__ __launch_bounds__(256) void select_blocks_kernel(SelArgs a) {
   const int lane = threadIdx.x & 63;
@@ -88,10 +136,15 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelArgs a) {
 #pragma unroll
     for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
 
+  // empty slots read key 0 (always present) and their scores are never used
+  int safe[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) safe[j] = cand[j] >= 0 ? cand[j] : 0;
+#pragma unroll 2
   for (int c = 0; c < a.d; ++c) {
     double kv[KPL];
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) kv[j] = cand[j] >= 0 ? kt[(int64_t)c * a.keys + cand[j]] : 0.0;
+    for (int j = 0; j < KPL; ++j) kv[j] = kt[(int64_t)c * a.keys + safe[j]];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const double qv = qp[i][c];
@@ -106,55 +159,145 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelArgs a) {
     if (!rvalid[i]) continue;
     // order-preserving keys, kept in the score registers
     uint64_t* key = reinterpret_cast<uint64_t*>(acc[i]);
-    int n_valid = 0;
+    bool valid[KPL], sel[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      key[j] = cand[j] >= 0 ? ordered_key(acc[i][j]) : 0ull;
-      n_valid += popc64(__ballot(cand[j] >= 0));
+      valid[j] = cand[j] >= 0;
+      key[j] = valid[j] ? ordered_key(acc[i][j]) : 0ull;
     }
-    const int k = a.topk;
-    uint64_t thr = 0;
-    bool exact = false;
-    if (n_valid == k) {
-      exact = true;  // every candidate is kept; keys of valid candidates are > 0
-      thr = 1;
-    } else {
-      for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t t = thr | (1ull << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) cnt += popc64(__ballot(cand[j] >= 0 && key[j] >= t));
-        if (cnt >= k) {
-          thr = t;
-          if (cnt == k) { exact = true; break; }
-        }
-      }
-    }
-    int need_eq = 0;
-    if (!exact) {
-      int gt = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) gt += popc64(__ballot(cand[j] >= 0 && key[j] > thr));
-      need_eq = k - gt;
-    }
-    int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row0 + i) * k;
-    int base = 0, eq_seen = 0;
+    wave_topk<KPL>(key, valid, a.topk, below, sel);
+    int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row0 + i) * a.topk;
+    int base = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      bool sel;
-      if (exact) {
-        sel = cand[j] >= 0 && key[j] >= thr;
-      } else {
-        const bool eq = cand[j] >= 0 && key[j] == thr;
-        const uint64_t em = __ballot(eq);
-        const int eq_rank = eq_seen + popc64(em & below);
-        eq_seen += popc64(em);
-        sel = (cand[j] >= 0 && key[j] > thr) || (eq && eq_rank < need_eq);
-      }
-      const uint64_t m = __ballot(sel);
-      if (sel) out[base + popc64(m & below)] = cand[j];
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) out[base + popc64(m & below)] = cand[j];
       base += popc64(m);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide rows (more than 1024 candidates, top-k <= 256): a workgroup per row.
+// Wave w scores the contiguous quarter [w*Q, (w+1)*Q) of the candidates and
+// keeps its own top-k; wave 0 then takes the top-k of the (at most 4k)
+// survivors, which are in ascending candidate order.  Anything in the row's
+// top-k is in its quarter's top-k under the same order, so the result is exact.
+// ---------------------------------------------------------------------------
+constexpr int WIDE_MAX_K = 256;
+
+template <int KPL>
+__global__ __launch_bounds__(256) void select_wide_kernel(SelArgs a) {
+  __shared__ uint64_t s_key[4][WIDE_MAX_K];
+  __shared__ int32_t s_cand[4][WIDE_MAX_K];
+  __shared__ int s_n[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hk = h / a.group;
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int qtr = (a.n_cand + 3) / 4;
+  const int c_lo = wave * qtr;
+  const int c_hi = min(a.n_cand, c_lo + qtr);
+
+  int cand[KPL];
+  if (a.parent) {
+    const int32_t* par = a.parent + (((int64_t)b * a.heads_q + h) * (a.rows / a.fanout) + row / a.fanout) * a.parent_k;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = c_lo + lane + 64 * j;
+      cand[j] = -1;
+      if (c < c_hi) {
+        const int32_t pv = par[c / a.fanout];
+        const int64_t key = (int64_t)pv * a.fanout + (c % a.fanout);
+        if (pv >= 0 && key < a.keys) cand[j] = (int)key;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = c_lo + lane + 64 * j;
+      cand[j] = c < c_hi ? c : -1;
+    }
+  }
+  int64_t qr = row;
+  if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + row];
+  if (qr < 0 || qr >= a.q_len) qr = 0;
+  qr = __builtin_amdgcn_readfirstlane((int)qr);
+  const double* qp = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
+
+  double acc[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) acc[j] = 0.0;
+  // empty slots read key 0 (always present) and their scores are never used
+  int safe[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) safe[j] = cand[j] >= 0 ? cand[j] : 0;
+#pragma unroll 2
+  for (int c = 0; c < a.d; ++c) {
+    const double qv = qp[c];
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kv[j] = kt[(int64_t)c * a.keys + safe[j]];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[j] = __builtin_fma(qv, kv[j], acc[j]);
+  }
+  uint64_t* key = reinterpret_cast<uint64_t*>(acc);
+  bool valid[KPL], sel[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    valid[j] = cand[j] >= 0;
+    key[j] = valid[j] ? ordered_key(acc[j]) : 0ull;
+  }
+  wave_topk<KPL>(key, valid, a.topk, below, sel);
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint64_t m = __ballot(sel[j]);
+    if (sel[j]) {
+      const int pos = base + popc64(m & below);
+      s_key[wave][pos] = key[j];
+      s_cand[wave][pos] = cand[j];
+    }
+    base += popc64(m);
+  }
+  if (lane == 0) s_n[wave] = base;
+  __syncthreads();
+  if (wave != 0) return;
+
+  // survivors of the four quarters, in ascending candidate order: at most 4 x 256
+  constexpr int KPL2 = 4 * WIDE_MAX_K / 64;
+  int off[5];
+  off[0] = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) off[w + 1] = off[w] + s_n[w];
+  uint64_t key2[KPL2];
+  bool valid2[KPL2], sel2[KPL2];
+  int cand2[KPL2];
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const int e = lane + 64 * j;
+    valid2[j] = e < off[4];
+    key2[j] = 0ull;
+    cand2[j] = -1;
+    if (valid2[j]) {
+      int w = 0;
+      while (e >= off[w + 1]) ++w;
+      key2[j] = s_key[w][e - off[w]];
+      cand2[j] = s_cand[w][e - off[w]];
+    }
+  }
+  wave_topk<KPL2>(key2, valid2, a.topk, below, sel2);
+  int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row) * a.topk;
+  base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const uint64_t m = __ballot(sel2[j]);
+    if (sel2[j]) out[base + popc64(m & below)] = cand2[j];
+    base += popc64(m);
   }
 }
 
@@ -172,37 +315,61 @@ hipError_t launch_kr(const SelArgs& a, int64_t batch, hipStream_t s) {
 // workgroup per batch entry; wave w sums tokens w, w+4, ...
 // ---------------------------------------------------------------------------
 template <typename T>
+__device__ __forceinline__ double sq_diff_row(const T* cur, const T* prev, int d) {
+  double s = 0.0;
+  for (int c = 0; c < d; c += 8) {
+    float x[8], y[8];
+    if constexpr (sizeof(T) == 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double df = (double)cur[c + i] - (double)prev[c + i];
+        s = __builtin_fma(df, df, s);
+      }
+      continue;
+    } else {
+      Vec8<T>::load(cur + c, x);
+      Vec8<T>::load(prev + c, y);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double df = (double)x[i] - (double)y[i];
+      s = __builtin_fma(df, df, s);
+    }
+  }
+  return s;
+}
+
+// Sixteen threads per token: thread g of a token sums the squared change of
+// heads g, g+16, ... over all channels; the sixteen partials are then added in
+// a fixed order, so the result does not depend on scheduling.
+template <typename T>
 __global__ __launch_bounds__(256) void select_change_kernel(const T* __restrict__ cur,
                                                             const T* __restrict__ prev, int heads,
                                                             int tokens, int d, int topk,
                                                             int32_t* __restrict__ idx) {
+  __shared__ double part[256];
   __shared__ double mse[1024];
   __shared__ int keep[1024];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < tokens; t += 4) {
+  const int g = threadIdx.x & 15;
+  for (int t0 = 0; t0 < tokens; t0 += 16) {
+    const int t = t0 + (threadIdx.x >> 4);
     double s = 0.0;
-    for (int h = 0; h < heads; ++h) {
-      const int64_t base = (((int64_t)b * heads + h) * tokens + t) * d;
-      for (int c = lane; c < d; c += 64) {
-        double x, y;
-        if constexpr (sizeof(T) == 2) {
-          x = (double)bf16_bits_to_f32(cur[base + c]);
-          y = (double)bf16_bits_to_f32(prev[base + c]);
-        } else {
-          x = (double)cur[base + c];
-          y = (double)prev[base + c];
-        }
-        const double df = x - y;
-        s = __builtin_fma(df, df, s);
+    if (t < tokens) {
+      for (int h = g; h < heads; h += 16) {
+        const int64_t base = (((int64_t)b * heads + h) * tokens + t) * d;
+        s += sq_diff_row<T>(cur + base, prev + base, d);
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) mse[t] = s / ((double)heads * (double)d);
+    part[threadIdx.x] = s;
+    __syncthreads();
+    if (g == 0 && t < tokens) {
+      double tot = 0.0;
+      for (int i = 0; i < 16; ++i) tot += part[threadIdx.x + i];
+      mse[t] = tot / ((double)heads * (double)d);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int t = threadIdx.x; t < tokens; t += 256) {
     const double v = mse[t];
     int rank = 0;
@@ -252,6 +419,11 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   if (kpl <= 4) return one_row ? launch_kr<4, 1>(a, d->batch, s) : launch_kr<4, 4>(a, d->batch, s);
   if (kpl <= 8) return one_row ? launch_kr<8, 1>(a, d->batch, s) : launch_kr<8, 4>(a, d->batch, s);
   if (kpl <= 16) return launch_kr<16, 1>(a, d->batch, s);
+  if (a.topk <= WIDE_MAX_K) {  // a workgroup per row, four quarters of at most 1024
+    dim3 grid((unsigned)a.rows, (unsigned)a.heads_q, (unsigned)d->batch);
+    select_wide_kernel<16><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (kpl <= 32) return launch_kr<32, 1>(a, d->batch, s);
   return launch_kr<64, 1>(a, d->batch, s);
 }

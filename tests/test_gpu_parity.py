@@ -127,11 +127,14 @@ def test_select_exact_ties_go_to_lower_index(basa):
     assert np.array_equal(got[0, 0, 0], np.arange(150))
 
 
-def test_select_gqa_row_map_and_wide_rows(basa):
-    note("select GQA 8/2 heads, row map, 4096 keys (top-128)")
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_gqa_row_map_and_wide_rows(basa, ties):
+    note(f"select GQA 8/2 heads, row map, 4096 keys (top-128), ties={ties}")
     g = np.random.Generator(np.random.PCG64(16))
     qf = g.standard_normal((1, 8, 16, 128))
     kbar = g.standard_normal((1, 2, 4096, 128))
+    if ties:  # 64 distinct key rows repeated: equal scores across the four quarters
+        kbar = np.tile(kbar[:, :, :64], (1, 1, 64, 1))
     rows = np.array([[1, 4, 7, 10, 13]], dtype=np.int32)
     idx = torch.empty(1, 8, 5, 128, dtype=torch.int32, device="cuda")
     basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 128,
@@ -247,7 +250,7 @@ def test_attn_generic_tiny_fp32(basa):
     assert max_err(lse, rl) <= 1e-5
 
 
-@pytest.mark.parametrize("tile_q", [16, 7, 32])
+@pytest.mark.parametrize("tile_q", [16, 7, 32, 1])
 def test_attn_segments_bias_and_f32_tables(basa, tile_q):
     note(f"attn segments: bf16 fine + f32 coarse tables, shifts, level bias, d64 tile {tile_q}")
     g = np.random.Generator(np.random.PCG64(24 + tile_q))
@@ -281,26 +284,54 @@ def test_attn_segments_bias_and_f32_tables(basa, tile_q):
     assert max_err(lse, rl) <= 1e-4
 
 
-def test_attn_generic_row_map_gqa_keeps_other_rows(basa):
-    note("attn generic: tile 1, q_rows, GQA 8/2, block16, top-8, in-place rows")
+@pytest.mark.parametrize("block_k", [16, 8])
+def test_attn_single_rows_row_map_gqa_keeps_other_rows(basa, block_k):
+    # block 16 runs the single-row kernel, block 8 the general one
+    note(f"attn tile 1, q_rows, GQA 8/2, block {block_k}, top-8, in-place rows")
     g = np.random.Generator(np.random.PCG64(25))
     d = 128
     q = wl.f32_to_bf16(g.standard_normal((1, 8, 16, d)).astype(np.float32))
     k = wl.f32_to_bf16(g.standard_normal((1, 2, 1024, d)).astype(np.float32))
     v = wl.f32_to_bf16(g.standard_normal((1, 2, 1024, d)).astype(np.float32))
     rows = np.array([[1, 4, 7, 10, 13]], dtype=np.int32)
-    idx = np.sort(np.stack([np.stack([g.choice(64, 8, replace=False) for _ in range(5)])
+    nblk = 1024 // block_k
+    idx = np.sort(np.stack([np.stack([g.choice(nblk, 8, replace=False) for _ in range(5)])
                             for _ in range(8)])[None], axis=-1).astype(np.int32)
+    idx[0, 3, 2, 5] = -1                                  # an empty slot
     o0 = g.standard_normal((1, 8, 16, d)).astype(np.float32)
     l0 = g.standard_normal((1, 8, 16)).astype(np.float32)
-    o, lse = run_attn(basa, q, [(idx, k, v, {})], 1, 16, 1 / math.sqrt(d), torch.float32,
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 1, block_k, 1 / math.sqrt(d), torch.float32,
                       q_rows=rows, o_init=o0, lse_init=l0)
-    ro, rl = orc.sparse_attention(q, k, v, idx, 1, 16, 1 / math.sqrt(d), q_rows=rows)
+    ro, rl = orc.sparse_attention(q, k, v, idx, 1, block_k, 1 / math.sqrt(d), q_rows=rows)
     act = np.zeros((1, 8, 16), dtype=bool)
     act[:, :, rows[0]] = True
     assert max_err(o[act], ro[act]) <= 1e-4 and max_err(lse[act], rl[act]) <= 1e-4
     assert np.array_equal(o[~act], o0[~act].astype(np.float64))
     assert np.array_equal(lse[~act], l0[~act].astype(np.float64))
+
+
+@pytest.mark.parametrize("block_k,d", [(16, 128), (32, 128), (48, 64)])
+def test_attn_single_rows_long_lists(basa, block_k, d):
+    # lists longer than 64 entries per wave share, several 16-key steps per
+    # entry, empty slots and one all-empty list; bf16 out
+    note(f"attn tile 1 long lists: block {block_k}, d {d}, 600 entries, GQA 8/2")
+    g = np.random.Generator(np.random.PCG64(26 + block_k))
+    nblk = 1200
+    q = wl.f32_to_bf16(g.standard_normal((1, 8, 3, d)).astype(np.float32))
+    k = wl.f32_to_bf16(g.standard_normal((1, 2, nblk * block_k, d)).astype(np.float32))
+    v = wl.f32_to_bf16(g.standard_normal((1, 2, nblk * block_k, d)).astype(np.float32))
+    idx = np.sort(np.stack([np.stack([g.choice(nblk, 600, replace=False) for _ in range(3)])
+                            for _ in range(8)])[None], axis=-1).astype(np.int32)
+    idx[0, 1, 0, ::7] = -1
+    idx[0, 6, 2, :] = -1
+    scale = 1 / math.sqrt(d)
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 1, block_k, scale, torch.bfloat16)
+    ro, rl = orc.sparse_attention(q, k, v, idx, 1, block_k, scale)
+    empty = np.zeros((1, 8, 3), dtype=bool)
+    empty[0, 6, 2] = True
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert max_err(o[~empty], ro[~empty]) <= O_TOL
+    assert max_err(lse[~empty], rl[~empty]) <= LSE_TOL
 
 
 # --------------------------------------------------------------------------- merge
