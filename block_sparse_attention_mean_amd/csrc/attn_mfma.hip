@@ -9,15 +9,20 @@
 // Work decomposition
 //   One workgroup (4 waves) computes one query tile of 128 rows; wave w owns
 //   rows 32w .. 32w+31.  Kept key blocks are streamed in stages of 64 keys
-//   (two stages per block).  Two workgroups share a CU (72 KB of LDS each),
-//   and as they synchronise only internally, one workgroup's softmax runs
-//   while the other's MFMAs do.
+//   (two stages per block).  Two workgroups share a CU (68 KB of LDS each).
 //   Per stage a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 //   (A = K rows from LDS, B = the wave's Q rows, held in registers for the
-//   whole walk), so each lane holds 32 logits of ONE query row: the row max and
-//   row sum need one cross-lane step (lane l and l^32).  Then O^T += V^T P^T
-//   with the same instruction (A = V^T from LDS, B = P taken straight from the
-//   S accumulators after a bf16 conversion).
+//   whole walk), so each lane holds 32 logits of ONE query row: the row max
+//   needs one cross-lane step (lane l and l^32, v_permlane32_swap).  Then
+//   O^T += V^T P^T with the same instruction (A = V^T read from LDS with the
+//   transposing ds_read_b64_tr_b16, B = P taken straight from the S
+//   accumulators after a bf16 conversion).
+//
+// Software pipeline.  Stage i issues the MFMAs of S(i+1) and, in the same
+// instruction stream, the softmax of S(i) (max, exp2, row sum, bf16 packing),
+// so the vector ALU works while the matrix core does; then the MFMAs of
+// O += P(i) V(i).  Scheduling groups interleave one MFMA with a few vector
+// and LDS instructions.
 //
 // Key permutation.  The 32x32 accumulator puts row rho of S^T in register
 // r = 4*(rho/8) + rho%4 of lane-half (rho/4)%2.  Loading key kappa into MFMA
@@ -25,16 +30,18 @@
 // half h hold keys 16c + 8h .. 16c + 8h + 7, which is exactly the B-operand
 // layout of a 16-key P chunk; the V^T operand reads the same keys.
 //
-// Data movement (double-buffered, one barrier per stage)
-//   K and V of the next stage are loaded into registers at the top of a stage
-//   and written to the other LDS buffer after the current stage's softmax, so
-//   the loads overlap the current stage's MFMA and softmax work.  (Direct
-//   global->LDS loads were tried: the compiler cannot prove that the DMA into
-//   one buffer does not alias reads of the other, and waits for the loads
-//   before every LDS read.)  K rows are 256 bytes whose 16-byte chunks are
-//   XOR-swizzled by the row number, so the 16 lanes reading one MFMA operand
-//   hit distinct banks; V is stored transposed, channel-major, in rows padded
-//   to 144 bytes (again conflict-free for the operand reads).
+// Data movement.  K and V stages go from global memory straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane, no registers): K(i+2) and
+// V(i+1) are requested at the top of stage i into the buffers that stage i-1
+// finished with, and one barrier per stage publishes them.  The four buffers
+// are separate LDS objects, so the compiler can tell the DMA targets from
+// the buffers being read and does not wait for the loads before each read.
+// Both layouts are permuted on the global side (each lane fetches the chunk
+// that belongs at its LDS slot):
+//   K: rows of 256 bytes, 16-byte chunk c of row r at chunk c ^ (r & 15), so
+//      the 16 lanes reading one MFMA operand hit distinct banks;
+//   V: rows of 256 bytes, chunk c of row r at chunk (c + 4 (r & 3)) & 15, so
+//      the four rows of one transposing read cover all banks once.
 //
 // Softmax: log2 domain with the scale folded in; the running max is only
 // raised when a stage's max exceeds it by more than 8 (a factor 256), so the
@@ -56,13 +63,24 @@ constexpr int BQ = 128;
 constexpr int BK = 128;
 constexpr int SK = 64;                        // keys per stage
 constexpr int NT = 256;                       // threads per workgroup (4 waves)
-constexpr int KBUF = SK * D * 2;              // 16 KB, swizzled rows of 256 B
-constexpr int VSTR = SK * 2 + 16;             // bytes per V^T row (one channel)
-constexpr int VBUF = D * VSTR;                // 18 KB
+constexpr int SBYTES = SK * D * 2;            // 16 KB per K or V stage
 constexpr int MAX_KEPT = 1024;                // list slots staged in LDS (the last holds the count)
-constexpr int LDS_BYTES = 2 * KBUF + 2 * VBUF + MAX_KEPT * 4;
 constexpr int RESIDENT_PER_XCD = 64;          // two workgroups per CU, 32 CUs per XCD
 constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
+
+#ifndef BASA_ATTN_GROUPS
+#define BASA_ATTN_GROUPS 0
+#endif
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__shared__ __attribute__((aligned(16))) uint8_t s_k0[SBYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_k1[SBYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_v0[SBYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_v1[SBYTES];
+__shared__ int32_t s_lst[MAX_KEPT];
 
 struct MfmaArgs {
   const uint16_t* q;
@@ -89,59 +107,173 @@ __device__ __forceinline__ int64_t tile_of(int64_t w, int64_t tiles) {
   return r * round_sz + xcd * RESIDENT_PER_XCD + s;
 }
 
-struct Stage {
-  uint4 k0, k1, k2, k3;  // K: 16-byte chunks tid + 256 i of the 64 x 256-byte stage
-  uint4 v0, v1, v2, v3;  // V: keys 4*(tid%16) .. +3, channels 8*(tid/16) .. +7
+template <int P> __device__ __forceinline__ uint8_t* kbuf() { return P ? s_k1 : s_k0; }
+template <int P> __device__ __forceinline__ uint8_t* vbuf() { return P ? s_v1 : s_v0; }
+
+// Per-thread state of the walk.
+struct Walk {
+  const uint16_t* kbase;   // this head's K rows
+  const uint16_t* vbase;
+  int koff[4], voff[4];    // element offsets of this lane's DMA chunks within a stage
+  int vrd[4];              // byte offsets of this lane's V^T operand reads (per 32-channel group)
+  int wave, krow_l, hi, n_stage;
 };
 
-__device__ __forceinline__ Stage load_stage(const uint16_t* kg, const uint16_t* vg, int tid) {
-  Stage s;
-  const uint16_t* kp = kg + (tid >> 4) * D + (tid & 15) * 8;
-  s.k0 = *reinterpret_cast<const uint4*>(kp);
-  s.k1 = *reinterpret_cast<const uint4*>(kp + 16 * D);
-  s.k2 = *reinterpret_cast<const uint4*>(kp + 32 * D);
-  s.k3 = *reinterpret_cast<const uint4*>(kp + 48 * D);
-  const uint16_t* vp = vg + (4 * (tid & 15)) * D + (tid >> 4) * 8;
-  s.v0 = *reinterpret_cast<const uint4*>(vp);
-  s.v1 = *reinterpret_cast<const uint4*>(vp + D);
-  s.v2 = *reinterpret_cast<const uint4*>(vp + 2 * D);
-  s.v3 = *reinterpret_cast<const uint4*>(vp + 3 * D);
-  return s;
+// first element of stage j (64 keys) of the head's K or V
+__device__ __forceinline__ int64_t stage_elem(int j) {
+  return ((int64_t)s_lst[j >> 1] * BK + (j & 1) * SK) * D;
 }
 
-__device__ __forceinline__ void store_stage(uint8_t* kbuf, uint8_t* vbuf, const Stage& s, int tid) {
-  // K: logical chunk c of row r sits at physical chunk c ^ (r & 15); rows r + 16 i share r & 15
-  const int r = tid >> 4, c = tid & 15;
-  const int off = r * 256 + ((c ^ (r & 15)) * 16);
-  *reinterpret_cast<uint4*>(kbuf + off) = s.k0;
-  *reinterpret_cast<uint4*>(kbuf + off + 16 * 256) = s.k1;
-  *reinterpret_cast<uint4*>(kbuf + off + 32 * 256) = s.k2;
-  *reinterpret_cast<uint4*>(kbuf + off + 48 * 256) = s.k3;
-  // V^T: channel 8*dg + 2j from the low halves, 8*dg + 2j + 1 from the high halves.
-  // v_perm_b32 selects bytes of {a:b}: 0x05040100 = low halves (b, a), 0x07060302 = high halves.
-  const int kgrp = tid & 15, dg = tid >> 4;
-  const uint32_t w0[4] = {s.v0.x, s.v0.y, s.v0.z, s.v0.w};
-  const uint32_t w1[4] = {s.v1.x, s.v1.y, s.v1.z, s.v1.w};
-  const uint32_t w2[4] = {s.v2.x, s.v2.y, s.v2.z, s.v2.w};
-  const uint32_t w3[4] = {s.v3.x, s.v3.y, s.v3.z, s.v3.w};
+template <int P>
+__device__ __forceinline__ void dma_k(const Walk& w, int j) {
+  const uint16_t* g = w.kbase + stage_elem(j);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint2 lo, hv;
-    lo.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
-    lo.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
-    hv.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
-    hv.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u);
-    *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j) * VSTR + 8 * kgrp) = lo;
-    *reinterpret_cast<uint2*>(vbuf + (8 * dg + 2 * j + 1) * VSTR + 8 * kgrp) = hv;
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(g + w.koff[i], (lds_void*)(kbuf<P>() + (16 * w.wave + 4 * i) * 256),
+                                     16, 0, 0);
+}
+
+template <int P>
+__device__ __forceinline__ void dma_v(const Walk& w, int j) {
+  const uint16_t* g = w.vbase + stage_elem(j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(g + w.voff[i], (lds_void*)(vbuf<P>() + (16 * w.wave + 4 * i) * 256),
+                                     16, 0, 0);
+}
+
+// S^T = K Q^T for the 64 keys in K buffer P (two 32-key sub-tiles)
+template <int P>
+__device__ __forceinline__ void qk(const Walk& w, const bf16x8* qf, f32x16* s) {
+  const uint8_t* kc = kbuf<P>();
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int krow = 32 * st + w.krow_l;
+    const uint8_t* rowp = kc + krow * 256;
+    f32x16 acc;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(rowp + (((2 * c + w.hi) ^ (krow & 15)) * 16));
+      if (c == 0) {
+        const f32x16 zero = {};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], zero, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], acc, 0, 0, 0);
+      }
+    }
+    s[st] = acc;
+  }
+}
+
+// Row max of one stage's logits (log2 units): raises m lazily and rescales l;
+// returns the factor the output accumulators still have to be scaled by.
+__device__ __forceinline__ float max_stage(const f32x16* s, float scale_log2, float& m, float& l) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+  const float m_new = mx > m + kLazy ? fmaxf(m, mx) : m;
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  m = m_new;
+  l *= alpha;
+  return alpha;
+}
+
+// P = exp2(scale*S - m) as bf16 MFMA operands; adds the row sum to l.
+__device__ __forceinline__ void exp_stage(const f32x16* s, float scale_log2, float m, float& l,
+                                          bf16x8* pf) {
+  float psum = 0.f;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * cc + j], scale_log2, -m));
+        psum += p;
+        pf[2 * st + cc][j] = (__bf16)p;
+      }
+  l += psum;
+}
+
+// O^T += V^T P^T over the 64 keys in V buffer P, 16 keys at a time
+template <int P>
+__device__ __forceinline__ void pv(const Walk& w, const bf16x8* pf, f32x16* oacc) {
+  const uint8_t* vc = vbuf<P>();
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {  // 16-key chunk: keys 16 ch .. 16 ch + 15
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint8_t* p0 = vc + 16 * ch * 256 + w.vrd[u];
+      const v4i16 k03 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+      const v4i16 k47 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * 256));
+      const bf16x8 vf =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(k03, k47, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], oacc[u], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void rescale(f32x16* oacc, float alpha) {
+  if (__ballot(alpha != 1.0f) != 0) {  // some row raised its max (wave-uniform branch)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+  }
+}
+
+// One stage i with buffer parity P = i & 1.  On entry S(i) is in s_cur with m
+// already raised for it (alpha: the pending rescale of O), K(i+1) sits in K
+// buffer P^1 and V(i) in V buffer P; S(i+1) goes to s_next.  NEXT: stage i+1
+// exists.
+template <int P, bool NEXT>
+__device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, const f32x16* s_cur,
+                                      f32x16* s_next, f32x16* oacc, float& m, float& l,
+                                      float& alpha, float scale_log2) {
+  if (NEXT) {
+    // K(i) and V(i-1) were consumed by stage i-1; past the end, K(n-1) is fetched again
+    dma_k<P>(w, min(i + 2, w.n_stage - 1));
+    dma_v<P ^ 1>(w, i + 1);
+  }
+  rescale(oacc, alpha);
+  bf16x8 pf[4];
+  if (NEXT) {
+    // S(i+1) on the matrix core while the vector unit exponentiates S(i)
+    qk<P ^ 1>(w, qf, s_next);
+    exp_stage(s_cur, scale_log2, m, l, pf);
+#if BASA_ATTN_GROUPS
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read (K operand)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU / transcendental
+    }
+#endif
+    // O += P(i) V(i) while the row max of S(i+1) is taken
+    pv<P>(w, pf, oacc);
+    alpha = max_stage(s_next, scale_log2, m, l);
+#if BASA_ATTN_GROUPS
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // transposing LDS reads (V operand)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 1);  // VALU
+    }
+#endif
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for stage i+1 has landed
+    __syncthreads();                     // ... and everyone's; buffers of stage i are free
+  } else {
+    exp_stage(s_cur, scale_log2, m, l, pf);
+    pv<P>(w, pf, oacc);
   }
 }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // K buffer i at smem + i*KBUF, V^T buffer i at smem + 2*KBUF + i*VBUF, list after them
-  int32_t* lst = reinterpret_cast<int32_t*>(smem + 2 * KBUF + 2 * VBUF);
-
   const int64_t tile = tile_of(blockIdx.x, a.tiles);
   const int64_t t = tile % a.lists;
   const int64_t bh = tile / a.lists;
@@ -151,19 +283,43 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
-  const int hi = lane >> 5;
 
-  const int64_t qrow = t * BQ + wave * 32 + li;
+  Walk w;
+  w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  w.hi = lane >> 5;
+  w.krow_l = swap_bits_2_3(li);
+  w.kbase = a.k + (b * a.heads_kv + hk) * a.len_k * D;
+  w.vbase = a.v + (b * a.heads_kv + hk) * a.len_k * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // DMA: lane lands at byte 16*lane of rows 16w+4i .. +3: row r, physical chunk p = lane & 15
+    const int r = 16 * w.wave + 4 * i + (lane >> 4);
+    const int p = lane & 15;
+    w.koff[i] = r * D + (p ^ (r & 15)) * 8;
+    w.voff[i] = r * D + ((p - 4 * (r & 3)) & 15) * 8;
+  }
+  {
+    // V^T operand: 16-lane group G, lane g: rows 8(G/2) + g/4 (+4), channels
+    // 32u + 16(G%2) + 4(g%4) .. +3 (bytes 8*(g&1) of logical chunk 4u + 2(G%2) + (g%4)/2)
+    const int G = lane >> 4, g = lane & 15;
+    const int row = 8 * (G >> 1) + (g >> 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cl = 4 * u + 2 * (G & 1) + ((g & 3) >> 1);
+      w.vrd[u] = row * 256 + ((cl + 4 * (row & 3)) & 15) * 16 + 8 * (g & 1);
+    }
+  }
+
+  const int64_t qrow = t * BQ + w.wave * 32 + li;
   const uint16_t* qp = a.q + ((b * a.heads_q + h) * a.len_q + qrow) * D;
   bf16x8 qf[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hi);
+  for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * w.hi);
 
   // compact the tile's list into LDS (valid blocks only, order kept): wave 0, 64 entries a step
   const int nblk_k = (int)(a.len_k / BK);
-  if (wave == 0) {
+  if (w.wave == 0) {
     const int32_t* g = a.kv_idx + ((b * a.heads_q + h) * a.idx_rows + t) * a.idx_stride;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int n = 0;
@@ -171,18 +327,15 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
       const int e = base + lane;
       const int32_t blk = e < a.kept ? g[e] : -1;
       const bool ok = blk >= 0 && blk < nblk_k;
-      const uint64_t m = __ballot(ok);
-      if (ok) lst[n + __popcll(m & below)] = blk;
-      n += __popcll(m);
+      const uint64_t msk = __ballot(ok);
+      if (ok) s_lst[n + __popcll(msk & below)] = blk;
+      n += __popcll(msk);
     }
-    if (lane == 0) lst[MAX_KEPT - 1] = n;  // kept < MAX_KEPT, so the count slot is never an entry
+    if (lane == 0) s_lst[MAX_KEPT - 1] = n;  // kept < MAX_KEPT, so the count slot is never an entry
   }
-  // settle the Q loads with a compiler-visible vmcnt(0): otherwise the wait-count
-  // bookkeeping at the loop head cannot tell them from the in-loop prefetches
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q loads settled (compiler-visible vmcnt(0))
   __syncthreads();
-  const int n_valid = lst[MAX_KEPT - 1];
-  const int n_stage = 2 * n_valid;
+  w.n_stage = 2 * s_lst[MAX_KEPT - 1];
 
   f32x16 oacc[4];
 #pragma unroll
@@ -192,95 +345,24 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   float m = -INFINITY;  // running row max of scale*log2(e)*logit (lazily raised)
   float l = 0.f;        // this lane's share of the running row sum
 
-  const uint16_t* kbase = a.k + (b * a.heads_kv + hk) * a.len_k * D;
-  const uint16_t* vbase = a.v + (b * a.heads_kv + hk) * a.len_k * D;
-  const int krow_l = swap_bits_2_3(li);
-
-  if (n_stage > 0) {
-    const int64_t off = (int64_t)lst[0] * BK * D;
-    const Stage s0 = load_stage(kbase + off, vbase + off, tid);
-    store_stage(smem, smem + 2 * KBUF, s0, tid);
-  }
-  __syncthreads();
-
-  for (int st_i = 0; st_i < n_stage; ++st_i) {
-    const int buf = st_i & 1;
-    const bool has_next = st_i + 1 < n_stage;
-    Stage nx;
-    if (has_next) {
-      const int sn = st_i + 1;
-      const int64_t off = (int64_t)lst[sn >> 1] * BK * D + (int64_t)(sn & 1) * SK * D;
-      nx = load_stage(kbase + off, vbase + off, tid);
+  if (w.n_stage > 0) {
+    // prologue: K(0), K(1), V(0); then S(0)
+    dma_k<0>(w, 0);
+    dma_k<1>(w, 1);
+    dma_v<0>(w, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    f32x16 s_a[2], s_b[2];  // logits of even / odd stages
+    qk<0>(w, qf, s_a);
+    float alpha = max_stage(s_a, a.scale_log2, m, l);
+    // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
+    int i = 0;
+    for (; i + 2 < w.n_stage; i += 2) {
+      stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, alpha, a.scale_log2);
+      stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, m, l, alpha, a.scale_log2);
     }
-
-    // S^T = K Q^T for the stage's two 32-key sub-tiles
-    const uint8_t* kcur = smem + buf * KBUF;
-    f32x16 s[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
-      const int krow = 32 * st + krow_l;
-      const uint8_t* rowp = kcur + krow * 256;
-      bf16x8 af[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        af[c] = *reinterpret_cast<const bf16x8*>(rowp + (((2 * c + hi) ^ (krow & 15)) * 16));
-      __builtin_amdgcn_sched_barrier(0);  // all 8 operand reads in flight before the chain
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c], qf[c], s[st], 0, 0, 0);
-    }
-
-    // online softmax in the log2 domain; lanes l and l^32 hold the same row
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    if (__ballot(mx > m + kLazy) != 0) {  // some row outgrew its max: rescale (wave-uniform)
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-      m = m_new;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], a.scale_log2, -m));
-        s[st][r] = p;
-        psum += p;
-      }
-    l += psum;
-
-    if (has_next)  // the other buffers were last read before the previous barrier
-      store_stage(smem + (buf ^ 1) * KBUF, smem + 2 * KBUF + (buf ^ 1) * VBUF, nx, tid);
-
-    // O^T += V^T P^T over the stage's 64 keys, 16 at a time
-    const uint8_t* vcur = smem + 2 * KBUF + buf * VBUF;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x8 pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[st][8 * cc + j];
-        const int key0 = 32 * st + 16 * cc + 8 * hi;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vcur + (32 * u + li) * VSTR + 2 * key0);
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[u], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // the current buffers are free; the next ones are complete
+    stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, alpha, a.scale_log2);
+    stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, m, l, alpha, a.scale_log2);
   }
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
@@ -291,7 +373,7 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int ch = 32 * u + 8 * rq + 4 * hi;
+      const int ch = 32 * u + 8 * rq + 4 * w.hi;
       const float v0 = oacc[u][4 * rq + 0] * inv, v1 = oacc[u][4 * rq + 1] * inv;
       const float v2 = oacc[u][4 * rq + 2] * inv, v3 = oacc[u][4 * rq + 3] * inv;
       if constexpr (OUT_BF16) {
@@ -304,7 +386,7 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
       }
     }
   }
-  if (hi == 0) a.lse[orow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (w.hi == 0) a.lse[orow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -340,15 +422,11 @@ hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int
   a.kept = g.count;
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
   if (a.tiles == 0) return hipSuccess;
-  const void* fn = o_dtype == BASA_BF16 ? (const void*)attn_mfma_kernel<true>
-                                        : (const void*)attn_mfma_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-  if (e != hipSuccess) return e;
   dim3 grid((unsigned)a.tiles);
   if (o_dtype == BASA_BF16)
-    attn_mfma_kernel<true><<<grid, NT, LDS_BYTES, s>>>(a);
+    attn_mfma_kernel<true><<<grid, NT, 0, s>>>(a);
   else
-    attn_mfma_kernel<false><<<grid, NT, LDS_BYTES, s>>>(a);
+    attn_mfma_kernel<false><<<grid, NT, 0, s>>>(a);
   return hipGetLastError();
 }
 
