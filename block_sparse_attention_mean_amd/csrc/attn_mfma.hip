@@ -19,10 +19,10 @@
 //   accumulators after a bf16 conversion).
 //
 // Software pipeline.  Stage i issues the MFMAs of S(i+1) and, in the same
-// instruction stream, the softmax of S(i) (max, exp2, row sum, bf16 packing),
-// so the vector ALU works while the matrix core does; then the MFMAs of
-// O += P(i) V(i).  Scheduling groups interleave one MFMA with a few vector
-// and LDS instructions.
+// instruction stream, the exponentials of S(i) (exp2, row sum, bf16
+// packing), so the vector ALU works while the matrix core does; then the
+// MFMAs of O += P(i) V(i) next to the row max of S(i+1), which fixes the max
+// (and the rescale of O) before stage i+1 starts.
 //
 // Key permutation.  The 32x32 accumulator puts row rho of S^T in register
 // r = 4*(rho/8) + rho%4 of lane-half (rho/4)%2.  Loading key kappa into MFMA
@@ -67,10 +67,6 @@ constexpr int SBYTES = SK * D * 2;            // 16 KB per K or V stage
 constexpr int MAX_KEPT = 1024;                // list slots staged in LDS (the last holds the count)
 constexpr int RESIDENT_PER_XCD = 64;          // two workgroups per CU, 32 CUs per XCD
 constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
-
-#ifndef BASA_ATTN_GROUPS
-#define BASA_ATTN_GROUPS 0
-#endif
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -142,26 +138,25 @@ __device__ __forceinline__ void dma_v(const Walk& w, int j) {
                                      16, 0, 0);
 }
 
-// S^T = K Q^T for the 64 keys in K buffer P (two 32-key sub-tiles)
+// S^T = K Q^T for the 64 keys in K buffer P: two 32-key sub-tiles whose
+// accumulation chains alternate, so consecutive MFMAs are independent
 template <int P>
 __device__ __forceinline__ void qk(const Walk& w, const bf16x8* qf, f32x16* s) {
   const uint8_t* kc = kbuf<P>();
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int krow = 32 * st + w.krow_l;
-    const uint8_t* rowp = kc + krow * 256;
-    f32x16 acc;
+  for (int c = 0; c < 8; ++c) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(rowp + (((2 * c + w.hi) ^ (krow & 15)) * 16));
+    for (int st = 0; st < 2; ++st) {
+      const int krow = 32 * st + w.krow_l;
+      const bf16x8 af =
+          *reinterpret_cast<const bf16x8*>(kc + krow * 256 + (((2 * c + w.hi) ^ (krow & 15)) * 16));
       if (c == 0) {
         const f32x16 zero = {};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], zero, 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], zero, 0, 0, 0);
       } else {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], acc, 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[c], s[st], 0, 0, 0);
       }
     }
-    s[st] = acc;
   }
 }
 
@@ -245,26 +240,10 @@ __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, co
     // S(i+1) on the matrix core while the vector unit exponentiates S(i)
     qk<P ^ 1>(w, qf, s_next);
     exp_stage(s_cur, scale_log2, m, l, pf);
-#if BASA_ATTN_GROUPS
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read (K operand)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU / transcendental
-    }
-#endif
     // O += P(i) V(i) while the row max of S(i+1) is taken
     pv<P>(w, pf, oacc);
     alpha = max_stage(s_next, scale_log2, m, l);
-#if BASA_ATTN_GROUPS
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // transposing LDS reads (V operand)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 2, 1);  // VALU
-    }
-#endif
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for stage i+1 has landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of stage i+1 have landed
     __syncthreads();                     // ... and everyone's; buffers of stage i are free
   } else {
     exp_stage(s_cur, scale_log2, m, l, pf);
@@ -363,6 +342,7 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
     }
     stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, alpha, a.scale_log2);
     stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, m, l, alpha, a.scale_log2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no load into this workgroup's LDS outlives it
   }
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
