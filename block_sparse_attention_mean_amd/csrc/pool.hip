@@ -40,6 +40,15 @@ template <> struct Load8<double> {
   }
 };
 
+// Workgroups go to the 8 XCDs round-robin; numbering them so that XCD x takes
+// the x-th contiguous eighth of the blocks keeps neighbouring blocks, whose
+// transposed means share cache lines, in one L2.
+__device__ __forceinline__ int64_t xcd_major(int64_t id, int64_t n) {
+  const int64_t per = n / 8;
+  if (id >= 8 * per) return id;  // the last n % 8 workgroups keep their number
+  return (id % 8) * per + id / 8;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int64_t len, int d,
                                                    int block, int64_t nb, int64_t n_wg,
@@ -47,8 +56,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int6
                                                    double* __restrict__ mean_cols,
                                                    void* __restrict__ mean_copy, int copy_dtype) {
   __shared__ double red[2048];  // [row groups][head_dim], row groups * head_dim == 2048
-  const int64_t wg = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
-  if (wg >= n_wg) return;
+  const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+  if (lin >= n_wg) return;
+  const int64_t wg = xcd_major(lin, n_wg);
   const int64_t o = wg / nb;
   const int64_t g = wg - o * nb;
   const int cols8 = d >> 3;
@@ -62,12 +72,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int6
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
   if (rg < groups) {
     int r = rg;
-    // four independent rows in flight per iteration
-    for (; r + 3 * groups < block; r += 4 * groups) {
-      Load8<T>::add(src + (int64_t)r * d, acc);
-      Load8<T>::add(src + (int64_t)(r + groups) * d, acc);
-      Load8<T>::add(src + (int64_t)(r + 2 * groups) * d, acc);
-      Load8<T>::add(src + (int64_t)(r + 3 * groups) * d, acc);
+    // eight independent rows in flight per iteration
+    for (; r + 7 * groups < block; r += 8 * groups) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Load8<T>::add(src + (int64_t)(r + u * groups) * d, acc);
     }
     for (; r < block; r += groups) Load8<T>::add(src + (int64_t)r * d, acc);
 #pragma unroll

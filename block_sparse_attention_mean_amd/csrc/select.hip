@@ -35,6 +35,12 @@ struct SelArgs {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+__device__ __forceinline__ uint64_t readfirstlane64(uint64_t x) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  return ((uint64_t)h << 32) | l;
+}
+
 // Wave-level top-k over KPL keys per lane in candidate order (lane + 64 j).
 // Marks sel[j] for the min(k, #valid) best under (key desc, candidate asc):
 // bitwise search from the top for the largest threshold T with at least k
@@ -51,9 +57,29 @@ __device__ __forceinline__ void wave_topk(const uint64_t* key, const bool* valid
     for (int j = 0; j < KPL; ++j) sel[j] = valid[j];
     return;
   }
-  uint64_t thr = 0;
+  // Every valid key lies in [lo, hi], so all share the bits above the highest
+  // bit where lo and hi differ: T has those bits, and the search starts below.
+  uint64_t hi = 0, lo = ~0ull;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    if (valid[j]) {
+      hi = key[j] > hi ? key[j] : hi;
+      lo = key[j] < lo ? key[j] : lo;
+    }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    const uint64_t ho = __shfl_xor(hi, sh), lw = __shfl_xor(lo, sh);
+    hi = ho > hi ? ho : hi;
+    lo = lw < lo ? lw : lo;
+  }
+  hi = readfirstlane64(hi);  // every lane holds the same value after the butterfly
+  lo = readfirstlane64(lo);
+  // diff == 0: all valid keys are equal, T = hi and the tie rule below takes the first k
+  const uint64_t diff = hi ^ lo;
+  const int top = diff ? 63 - __clzll(diff) : -1;
+  uint64_t thr = top >= 63 ? 0 : (hi >> (top + 1)) << (top + 1);
   bool exact = false;
-  for (int bit = 63; bit >= 0; --bit) {
+  for (int bit = top; bit >= 0; --bit) {
     const uint64_t t = thr | (1ull << bit);
     int cnt = 0;
 #pragma unroll
@@ -301,6 +327,235 @@ __global__ __launch_bounds__(256) void select_wide_kernel(SelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Channel-split rows (257..512 candidates, no parent list): a workgroup per
+// four rows of one head.  Wave w forms the partial scores of all four rows over
+// its quarter of the channels (a short chain of dependent loads instead of a
+// long one), the partials meet in LDS, and wave w completes row w - adding the
+// four quarters in the fixed order 0, 1, 2, 3 - and takes its top-k.
+// ---------------------------------------------------------------------------
+// Workgroups go to the 8 XCDs round-robin; numbering them so that XCD x takes
+// the x-th contiguous eighth of the (batch, head, row group) space keeps each
+// head's key means in one XCD's L2.
+__device__ __forceinline__ int64_t xcd_major(int64_t id, int64_t n) {
+  const int64_t per = n / 8;
+  if (id >= 8 * per) return id;  // the last n % 8 workgroups keep their number
+  return (id % 8) * per + id / 8;
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void select_split_kernel(SelArgs a, int64_t groups) {
+  __shared__ double part[4][3][KPL * 64];  // [writer wave][other row][slot]: 3 rows per writer
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (b, h, row group) from the XCD-major workgroup number
+  const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+  const int64_t rg = unit % groups;
+  const int h = (int)((unit / groups) % a.heads_q);
+  const int b = (int)(unit / (groups * a.heads_q));
+  const int64_t row0 = rg * 4;
+  const int hk = h / a.group;
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+
+  int cand[KPL], safe[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int c = lane + 64 * j;
+    cand[j] = c < a.n_cand ? c : -1;
+    safe[j] = c < a.n_cand ? c : 0;  // empty slots read key 0; their scores are never used
+  }
+  const double* qp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t qr = row0 + i < a.rows ? row0 + i : row0;
+    if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + qr];
+    if (qr < 0 || qr >= a.q_len) qr = 0;  // a row map entry outside q reads row 0
+    qr = __builtin_amdgcn_readfirstlane((int)qr);
+    qp[i] = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
+  }
+
+  double acc[4][KPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
+  const int cq = a.d / 4;
+  const int c0 = wave * cq;
+#pragma unroll 4
+  for (int c = c0; c < c0 + cq; ++c) {
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kv[j] = kt[(int64_t)c * a.keys + safe[j]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double qv = qp[i][c];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
+    }
+  }
+  // hand the other rows' partials over
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i == wave) continue;
+    const int slot = i < wave ? i : i - 1;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) part[wave][slot][j * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  const int64_t row = row0 + wave;
+  if (row >= a.rows) return;
+  double sc[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    double tot = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      double pv;
+      if (v == wave) {
+        // own partial: the registers of row `wave` (a wave-uniform choice among four)
+        pv = wave == 0 ? acc[0][j] : wave == 1 ? acc[1][j] : wave == 2 ? acc[2][j] : acc[3][j];
+      } else {
+        pv = part[v][wave < v ? wave : wave - 1][j * 64 + lane];
+      }
+      tot = v == 0 ? pv : tot + pv;
+    }
+    sc[j] = tot;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t key[KPL];
+  bool valid[KPL], sel[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    valid[j] = cand[j] >= 0;
+    key[j] = valid[j] ? ordered_key(sc[j]) : 0ull;
+  }
+  wave_topk<KPL>(key, valid, a.topk, below, sel);
+  int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row) * a.topk;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint64_t m = __ballot(sel[j]);
+    if (sel[j]) out[base + popc64(m & below)] = cand[j];
+    base += popc64(m);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged rows (exactly 64*KPL keys, no parent list): a workgroup per 32
+// rows of one head, eight per wave.  The key means are read once per
+// workgroup: chunks of 8 channels x all keys go from global memory straight
+// into LDS (double-buffered, one barrier per chunk), and the four waves take
+// their key values from there; every key value feeds eight rows.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int SEL_CH = 8;  // channels per staged chunk
+
+template <int KPL>
+struct SelStage {
+  static constexpr int BYTES = SEL_CH * KPL * 64 * 8;
+};
+__shared__ __attribute__((aligned(16))) uint8_t s_sel0[SelStage<8>::BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_sel1[SelStage<8>::BYTES];
+
+template <int KPL, int P>
+__device__ __forceinline__ void sel_dma(const double* src) {
+  uint8_t* dst = P ? s_sel1 : s_sel0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int i = 0; i < SelStage<KPL>::BYTES / 4096; ++i)
+    __builtin_amdgcn_global_load_lds(src + (i * 4096 + tid * 16) / 8,
+                                     (lds_void*)(dst + i * 4096 + wave * 1024), 16, 0, 0);
+}
+
+constexpr int SEL_RW = 8;  // rows per wave
+
+template <int KPL, int P>
+__device__ __forceinline__ void sel_chunk(const double* const* qp, int c0, double (*acc)[KPL]) {
+  const double* kc = reinterpret_cast<const double*>(P ? s_sel1 : s_sel0);
+  const int lane = threadIdx.x & 63;
+#pragma unroll 2
+  for (int cc = 0; cc < SEL_CH; ++cc) {
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kv[j] = kc[cc * KPL * 64 + lane + 64 * j];
+#pragma unroll
+    for (int i = 0; i < SEL_RW; ++i) {
+      const double qv = qp[i][c0 + cc];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
+    }
+  }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256, 2) void select_lds_kernel(SelArgs a, int64_t groups) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+  const int64_t rg = unit % groups;
+  const int h = (int)((unit / groups) % a.heads_q);
+  const int b = (int)(unit / (groups * a.heads_q));
+  const int64_t row0 = (rg * 4 + wave) * SEL_RW;
+  const int hk = h / a.group;
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+
+  const double* qp[SEL_RW];
+#pragma unroll
+  for (int i = 0; i < SEL_RW; ++i) {
+    int64_t qr = row0 + i < a.rows ? row0 + i : (row0 < a.rows ? row0 : 0);
+    if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + qr];
+    if (qr < 0 || qr >= a.q_len) qr = 0;  // a row map entry outside q reads row 0
+    qr = __builtin_amdgcn_readfirstlane((int)qr);
+    qp[i] = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
+  }
+  double acc[SEL_RW][KPL];
+#pragma unroll
+  for (int i = 0; i < SEL_RW; ++i)
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
+
+  // chunks of SEL_CH channels; head_dim / SEL_CH is even (checked at launch)
+  const int n_chunk = a.d / SEL_CH;
+  const int64_t chunk_elems = (int64_t)SEL_CH * a.keys;
+  sel_dma<KPL, 0>(kt);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int k = 0; k < n_chunk; k += 2) {
+    sel_dma<KPL, 1>(kt + (k + 1) * chunk_elems);
+    sel_chunk<KPL, 0>(qp, k * SEL_CH, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (k + 2 < n_chunk) sel_dma<KPL, 0>(kt + (k + 2) * chunk_elems);
+    sel_chunk<KPL, 1>(qp, (k + 1) * SEL_CH, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < SEL_RW; ++i) {
+    const int64_t row = row0 + i;
+    if (row >= a.rows) continue;
+    uint64_t key[KPL];
+    bool valid[KPL], sel[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      valid[j] = true;
+      key[j] = ordered_key(acc[i][j]);
+    }
+    wave_topk<KPL>(key, valid, a.topk, below, sel);
+    int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row) * a.topk;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) out[base + popc64(m & below)] = lane + 64 * j;
+      base += popc64(m);
+    }
+  }
+}
+
 template <int KPL, int RW>
 hipError_t launch_kr(const SelArgs& a, int64_t batch, hipStream_t s) {
   const int64_t rows_per_wg = 4 * RW;
@@ -417,6 +672,18 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   if (kpl <= 1) return one_row ? launch_kr<1, 1>(a, d->batch, s) : launch_kr<1, 4>(a, d->batch, s);
   if (kpl <= 2) return one_row ? launch_kr<2, 1>(a, d->batch, s) : launch_kr<2, 4>(a, d->batch, s);
   if (kpl <= 4) return one_row ? launch_kr<4, 1>(a, d->batch, s) : launch_kr<4, 4>(a, d->batch, s);
+  if (!d->parent && a.keys == 512 && a.d % (2 * SEL_CH) == 0) {  // LDS-staged key means
+    const int64_t groups = (a.rows + 4 * SEL_RW - 1) / (4 * SEL_RW);
+    dim3 grid((unsigned)(groups * a.heads_q * d->batch), 1);
+    select_lds_kernel<8><<<grid, 256, 0, s>>>(a, groups);
+    return hipGetLastError();
+  }
+  if (kpl > 4 && kpl <= 8 && !d->parent && a.d % 4 == 0) {  // channel-split rows
+    const int64_t groups = (a.rows + 3) / 4;
+    dim3 grid((unsigned)(groups * a.heads_q * d->batch), 1);
+    select_split_kernel<8><<<grid, 256, 0, s>>>(a, groups);
+    return hipGetLastError();
+  }
   if (kpl <= 8) return one_row ? launch_kr<8, 1>(a, d->batch, s) : launch_kr<8, 4>(a, d->batch, s);
   if (kpl <= 16) return launch_kr<16, 1>(a, d->batch, s);
   if (a.topk <= WIDE_MAX_K) {  // a workgroup per row, four quarters of at most 1024

@@ -144,6 +144,33 @@ def test_select_gqa_row_map_and_wide_rows(basa, ties):
     assert np.array_equal(host(idx), ref)
 
 
+@pytest.mark.parametrize("keys,d,row_map", [(300, 64, False), (512, 128, False), (449, 128, True),
+                                             (512, 64, True)])
+def test_select_channel_split_rows(basa, keys, d, row_map):
+    # 257..511 candidates run the channel-split kernel, exactly 512 the LDS-staged
+    # one: 37 rows (ragged last groups), GQA 4/2, duplicated key columns and an
+    # all-zero query row
+    note(f"select channel-split: {keys} keys, d {d}, row map {row_map}, ties")
+    g = np.random.Generator(np.random.PCG64(18 + keys))
+    q_len = 40 if row_map else 37
+    qf = g.standard_normal((1, 4, q_len, d))
+    qf[0, 1, 5] = 0.0
+    kbar = g.standard_normal((1, 2, keys, d))
+    kbar[:, :, 200] = kbar[:, :, 7]
+    kbar[:, :, 250] = kbar[:, :, 7]
+    rows = None
+    if row_map:
+        rows = np.sort(g.choice(q_len, 37, replace=False))[None].astype(np.int32)
+        rows[0, 3] = 5
+    idx = torch.empty(1, 4, 37, 64, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 64,
+                     scale=1 / math.sqrt(d), q_rows=dev(rows) if row_map else None)
+    torch.cuda.synchronize()
+    qsel = qf[:, :, rows[0]] if row_map else qf
+    ref = orc.topk_ascending(orc.block_logits(qsel, kbar, 1 / math.sqrt(d)), 64)
+    assert np.array_equal(host(idx), ref)
+
+
 def test_select_children_of_parent_picks(basa):
     note("select candidate mode: 256 rows, parent top-8 x fanout 16")
     g = np.random.Generator(np.random.PCG64(17))
