@@ -133,6 +133,8 @@ int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int 
       return from_hip(basa::launch_attn_mfma(d, q, o, o_dtype, lse, s));
     if (basa::attn_row_supported(d))
       return from_hip(basa::launch_attn_row(d, q, q_dtype, o, o_dtype, lse, s));
+    if (basa::attn_t16_supported(d, q_dtype))
+      return from_hip(basa::launch_attn_t16(d, q, o, o_dtype, lse, s));
     if (basa::attn_tile_supported(d))
       return from_hip(basa::launch_attn_tile(d, q, q_dtype, o, o_dtype, lse, s));
     return from_hip(basa::launch_attn_generic(d, q, q_dtype, o, o_dtype, lse, s));

@@ -85,6 +85,9 @@ hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int
 bool attn_row_supported(const basa_attn_desc* d);
 hipError_t launch_attn_row(const basa_attn_desc* d, const void* q, int q_dtype, void* o,
                            int o_dtype, float* lse, hipStream_t s);
+bool attn_t16_supported(const basa_attn_desc* d, int q_dtype);
+hipError_t launch_attn_t16(const basa_attn_desc* d, const void* q, void* o, int o_dtype, float* lse,
+                           hipStream_t s);
 bool attn_tile_supported(const basa_attn_desc* d);
 hipError_t launch_attn_tile(const basa_attn_desc* d, const void* q, int q_dtype, void* o,
                             int o_dtype, float* lse, hipStream_t s);

@@ -307,8 +307,48 @@ def test_attn_segments_bias_and_f32_tables(basa, tile_q):
     bias = np.concatenate([np.zeros(i0.shape), np.full(i1.shape[:2] + (tiles, 3), b1),
                            np.full(i2.shape[:2] + (tiles, 1), b2)], axis=-1)
     ro, rl = orc.sparse_attention(q, kt, vt, full, tile_q, blk, 0.125, bias=bias)
-    assert max_err(o, ro) <= 1e-4
-    assert max_err(lse, rl) <= 1e-4
+    # 16-row tiles run on bf16 MFMA (P rounded to bf16): the bf16 bar; the other
+    # tile sizes run in float32 throughout
+    o_tol, lse_tol = (O_TOL, LSE_TOL) if tile_q == 16 else (1e-4, 1e-4)
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    assert eo <= o_tol, eo
+    assert el <= lse_tol, el
+
+
+@pytest.mark.parametrize("d,row_map", [(128, False), (128, True), (64, True)])
+def test_attn_16_row_tiles_f32_tables_row_map(basa, d, row_map):
+    # 16-row tiles over 16-key blocks run the tile MFMA kernel: a bf16 segment and a
+    # float32 segment with a bias, GQA 4/2, empty slots, optionally a row map, bf16 out
+    note(f"attn 16-row tiles: d {d}, row map {row_map}, bf16 + f32 tables")
+    g = np.random.Generator(np.random.PCG64(27 + d + row_map))
+    n_q, tiles, nk = 320, 12, 512
+    q = wl.f32_to_bf16(g.standard_normal((1, 4, n_q, d)).astype(np.float32))
+    kb = wl.f32_to_bf16(g.standard_normal((1, 2, nk, d)).astype(np.float32))
+    vb = wl.f32_to_bf16(g.standard_normal((1, 2, nk, d)).astype(np.float32))
+    kf = g.standard_normal((1, 2, 64, d)).astype(np.float32)
+    vf = g.standard_normal((1, 2, 64, d)).astype(np.float32)
+    i0 = np.sort(g.integers(0, nk // 16, (1, 4, tiles, 6)), axis=-1).astype(np.int32)
+    i0[0, 2, 3, 1] = -1
+    i1 = np.sort(g.integers(0, 4, (1, 4, tiles, 3)), axis=-1).astype(np.int32)
+    i1[0, 1, 5, :] = -1                                   # a segment list with no block
+    rows = None
+    if row_map:
+        rows = np.stack([np.sort(g.choice(n_q, tiles * 16, replace=False))])[None][0].astype(np.int32)
+    else:
+        q = q[:, :, :tiles * 16]
+    b1 = math.log(16)
+    segs = [(i0, kb, vb, {}), (i1, kf, vf, {"bias": b1})]
+    o, lse = run_attn(basa, q, segs, 16, 16, 1 / math.sqrt(d), torch.bfloat16, q_rows=rows)
+    kt = np.concatenate([orc.as_f64(kb), kf.astype(np.float64)], axis=2)
+    vt = np.concatenate([orc.as_f64(vb), vf.astype(np.float64)], axis=2)
+    full = np.concatenate([i0, np.where(i1 >= 0, i1 + nk // 16, -1)], axis=-1)
+    bias = np.concatenate([np.zeros(i0.shape), np.full(i1.shape, b1)], axis=-1)
+    ro, rl = orc.sparse_attention(q, kt, vt, full, 16, 16, 1 / math.sqrt(d), bias=bias, q_rows=rows)
+    sel = ~np.isnan(rl)
+    assert sel.sum() == 4 * tiles * 16
+    eo, el = max_err(o[sel], ro[sel]), max_err(lse[sel], rl[sel])
+    assert eo <= O_TOL, eo
+    assert el <= LSE_TOL, el
 
 
 @pytest.mark.parametrize("block_k", [16, 8])
