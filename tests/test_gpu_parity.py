@@ -250,6 +250,25 @@ def test_attn_mfma_small_with_empty_slots(basa, o_dtype):
     assert max_err(lse[~empty], rl[~empty]) <= LSE_TOL
 
 
+def test_attn_mfma_batch2_gqa(basa):
+    # the MFMA kernel with two batch entries and grouped key heads (4 query heads on
+    # 2 key heads), lists of different lengths padded with -1
+    note("attn mfma: batch 2, GQA 4/2, L 1024, kept 3 of 8 with padding")
+    g = np.random.Generator(np.random.PCG64(29))
+    q = wl.f32_to_bf16(g.standard_normal((2, 4, 1024, 128)).astype(np.float32))
+    k = wl.f32_to_bf16(g.standard_normal((2, 2, 1024, 128)).astype(np.float32))
+    v = wl.f32_to_bf16(g.standard_normal((2, 2, 1024, 128)).astype(np.float32))
+    idx = np.sort(np.stack([np.stack([np.stack([g.choice(8, 3, replace=False) for _ in range(8)])
+                                      for _ in range(4)]) for _ in range(2)]), axis=-1).astype(np.int32)
+    idx[1, 3, 7, 0] = -1
+    idx[0, 1, 2, 2] = -1
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 128, 128, 1 / math.sqrt(128), torch.bfloat16)
+    ro, rl = orc.sparse_attention(q, k, v, idx, 128, 128, 1 / math.sqrt(128))
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    assert eo <= O_TOL, eo
+    assert el <= LSE_TOL, el
+
+
 def test_attn_mfma_dlm16k_sampled_and_deterministic(basa):
     note("attn mfma dlm16k: oracle lists, 48 sampled tiles, repeat-run bitwise")
     w = wl.WORKLOADS["dlm16k"]
