@@ -7,8 +7,9 @@
 // segments with an additive logit bias per level.  Online softmax per 16-key
 // block.
 //
-// One wave computes one tile; a workgroup holds four independent waves (no
-// barriers).  Per 16-key block the wave forms S^T = K Q^T with
+// One wave computes one tile; a workgroup holds four waves.  Float32 segments
+// whose list row is shared by the workgroup's four tiles are staged once per
+// workgroup (barrier-synchronised); everything else each wave walks alone.  Per 16-key block the wave forms S^T = K Q^T with
 // v_mfma_f32_16x16x16bf16_1k: lane l holds the logits of query row l%16 for
 // keys 4(l/16) .. +3, which is exactly the B operand (P^T) of the next
 // O^T += V^T P^T; V^T comes from the wave's LDS area through the transposing
@@ -52,6 +53,7 @@ struct T16Args {
   const int32_t* q_rows;
   int64_t len_q, lists, tiles;
   int heads_q, heads_kv, group;
+  int share;  // lists % NW == 0: the NW tiles of a workgroup share list rows with shift >= 2
   float scale_log2;
 };
 
@@ -105,45 +107,15 @@ struct T16Lds {
   static constexpr int BYTES = 2 * HALF;
 };
 
-// One 16-key block: logits, online softmax, O update.  kr: this lane's key row
-// relative to the head, or -1 when the key does not exist.
-template <int D, bool BF>
-__device__ __forceinline__ void t16_block(const Raw<D, BF>& kraw, const Raw<D, BF>& vraw, bool kvalid,
-                                          const v4i16* qb, float scale_log2, float bias_log2,
-                                          uint8_t* lds, T16State<D>& st) {
-  constexpr int CPL = D / 4;
-  constexpr int STEPS = CPL / 4;
+// Online softmax of one block's logits (lane l: query row l%16, keys
+// 4(l/16)+i) and O^T += V^T P^T with V^T from an LDS value area (the hi half,
+// and with LO the lo half at +HALF).  kvalid: this lane's key (l%16) exists.
+template <int D, bool LO>
+__device__ __forceinline__ void t16_softmax_pv(const f32x4& s, bool kvalid, float scale_log2,
+                                               float bias_log2, const uint8_t* varea,
+                                               T16State<D>& st) {
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
-  // value rows -> LDS (row l%16 = key, channels CPL*G .. +CPL-1), hi and lo halves
-  {
-    uint8_t* rowp = lds + (lane & 15) * T16Lds<D>::STRIDE + CPL * G * 2;
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < Raw<D, BF>::N / 4; ++i) *reinterpret_cast<uint4*>(rowp + 16 * i) = vraw.word4(i);
-    } else {
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        uint2 hi, lo;
-        split4(vraw.f(4 * s), vraw.f(4 * s + 1), vraw.f(4 * s + 2), vraw.f(4 * s + 3), hi, lo);
-        *reinterpret_cast<uint2*>(rowp + 8 * s) = hi;
-        *reinterpret_cast<uint2*>(rowp + T16Lds<D>::HALF + 8 * s) = lo;
-      }
-    }
-  }
-  // S^T = K Q^T (16 keys x 16 query rows)
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int st_ = 0; st_ < STEPS; ++st_) {
-    if constexpr (BF) {
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kraw.b4(st_), qb[st_], s, 0, 0, 0);
-    } else {
-      uint2 hi, lo;
-      split4(kraw.f(4 * st_), kraw.f(4 * st_ + 1), kraw.f(4 * st_ + 2), kraw.f(4 * st_ + 3), hi, lo);
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, hi), qb[st_], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, lo), qb[st_], s, 0, 0, 0);
-    }
-  }
   // keys 4G+i of this lane's query row; a key that does not exist has logit -inf
   // (the lane's own kvalid flag is for key l%16: fetch the flags of keys 4G+i)
   float z[4];
@@ -171,19 +143,64 @@ __device__ __forceinline__ void t16_block(const Raw<D, BF>& kraw, const Raw<D, B
     st.l += p[i];
   }
   const v4i16 pb = __builtin_bit_cast(v4i16, make_uint2(pack2(p[0], p[1]), pack2(p[2], p[3])));
-  // O^T += V^T P^T: lane r of group G reads value row 4G + r/4, channels 16cb + 4(r%4) .. +3
+  // lane r of group G reads value row 4G + r/4, channels 16cb + 4(r%4) .. +3
   const int g = lane & 15;
-  const uint8_t* vb = lds + (4 * G + (g >> 2)) * T16Lds<D>::STRIDE + 8 * (g & 3);
+  const uint8_t* vb = varea + (4 * G + (g >> 2)) * T16Lds<D>::STRIDE + 8 * (g & 3);
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) {
     const v4i16 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 32 * cb));
     st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vhi, pb, st.o[cb], 0, 0, 0);
-    if constexpr (!BF) {
+    if constexpr (LO) {
       const v4i16 vlo =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + T16Lds<D>::HALF + 32 * cb));
       st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vlo, pb, st.o[cb], 0, 0, 0);
     }
   }
+}
+
+// Key or value rows of one block (this lane: row l%16, its channel run) into an
+// LDS area, as bf16 (hi half; float32 rows also get the lo half at +HALF).
+template <int D, bool BF>
+__device__ __forceinline__ void t16_store_rows(const Raw<D, BF>& raw, uint8_t* area) {
+  constexpr int CPL = D / 4;
+  const int lane = threadIdx.x & 63;
+  uint8_t* rowp = area + (lane & 15) * T16Lds<D>::STRIDE + CPL * (lane >> 4) * 2;
+  if constexpr (BF) {
+#pragma unroll
+    for (int i = 0; i < Raw<D, BF>::N / 4; ++i) *reinterpret_cast<uint4*>(rowp + 16 * i) = raw.word4(i);
+  } else {
+#pragma unroll
+    for (int s = 0; s < CPL / 4; ++s) {
+      uint2 hi, lo;
+      split4(raw.f(4 * s), raw.f(4 * s + 1), raw.f(4 * s + 2), raw.f(4 * s + 3), hi, lo);
+      *reinterpret_cast<uint2*>(rowp + 8 * s) = hi;
+      *reinterpret_cast<uint2*>(rowp + T16Lds<D>::HALF + 8 * s) = lo;
+    }
+  }
+}
+
+// One 16-key block of this wave's own list: logits from the key rows in
+// registers, values through the wave's LDS area.
+template <int D, bool BF>
+__device__ __forceinline__ void t16_block(const Raw<D, BF>& kraw, const Raw<D, BF>& vraw, bool kvalid,
+                                          const v4i16* qb, float scale_log2, float bias_log2,
+                                          uint8_t* lds, T16State<D>& st) {
+  constexpr int STEPS = D / 16;
+  t16_store_rows<D, BF>(vraw, lds);
+  // S^T = K Q^T (16 keys x 16 query rows)
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st_ = 0; st_ < STEPS; ++st_) {
+    if constexpr (BF) {
+      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kraw.b4(st_), qb[st_], s, 0, 0, 0);
+    } else {
+      uint2 hi, lo;
+      split4(kraw.f(4 * st_), kraw.f(4 * st_ + 1), kraw.f(4 * st_ + 2), kraw.f(4 * st_ + 3), hi, lo);
+      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, hi), qb[st_], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, lo), qb[st_], s, 0, 0, 0);
+    }
+  }
+  t16_softmax_pv<D, !BF>(s, kvalid, scale_log2, bias_log2, lds, st);
 }
 
 // This lane's key (l%16 of list entry j) relative to the head, or -1.
@@ -234,16 +251,87 @@ __device__ __forceinline__ void t16_segment(float scale_log2, const T16Seg& sg, 
   }
 }
 
+// A float32 segment whose list row is the same for all NW tiles of the
+// workgroup (the log-linear coarse levels): the workgroup walks it together,
+// NW blocks per chunk.  Wave w loads block w of the chunk, splits it into bf16
+// hi/lo and stores keys and values in slot w of the shared LDS area; after a
+// barrier every wave reduces all NW slots for its own rows.  Each coarse block
+// is thus read and split once per workgroup instead of once per tile.  The
+// next chunk's rows are loaded while the current chunk is reduced.
+template <int D>
+struct T16Shared {
+  static constexpr int SLOT = 4 * T16Lds<D>::HALF;  // keys hi, keys lo, values hi, values lo
+  static constexpr int BYTES = NW * SLOT;
+};
+
+template <int D>
+__device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Seg& sg,
+                                                   const int32_t* lst, int64_t head_row,
+                                                   const v4i16* qb, uint8_t* shared,
+                                                   T16State<D>& st) {
+  constexpr int CPL = D / 4;
+  constexpr int HALF = T16Lds<D>::HALF;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ch0 = CPL * (lane >> 4);
+  const int n = sg.count;
+  Raw<D, false> kr, vr;
+  {
+    const int64_t rr = wave < n ? t16_row(lst, wave, sg.len) : -1;
+    const int64_t r = head_row + (rr >= 0 ? rr : 0);
+    kr.load(sg.k, r * D + ch0);
+    vr.load(sg.v, r * D + ch0);
+  }
+  for (int c0 = 0; c0 < n; c0 += NW) {
+    uint8_t* slot = shared + wave * T16Shared<D>::SLOT;
+    t16_store_rows<D, false>(kr, slot);
+    t16_store_rows<D, false>(vr, slot + 2 * HALF);
+    __syncthreads();
+    if (c0 + NW < n) {  // next chunk's rows
+      const int j = c0 + NW + wave;
+      const int64_t rr = j < n ? t16_row(lst, j, sg.len) : -1;
+      const int64_t r = head_row + (rr >= 0 ? rr : 0);
+      kr.load(sg.k, r * D + ch0);
+      vr.load(sg.v, r * D + ch0);
+    }
+    for (int b = 0; b < NW; ++b) {
+      const int j = c0 + b;
+      if (j >= n) break;
+      const int32_t blk = lst[j];
+      if (blk < 0) continue;  // an unused list slot (wave-uniform)
+      const bool kvalid = (int64_t)blk * 16 + (lane & 15) < sg.len;
+      const uint8_t* ks = shared + b * T16Shared<D>::SLOT + (lane & 15) * T16Lds<D>::STRIDE + ch0 * 2;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st_ = 0; st_ < CPL / 4; ++st_) {
+        const v4i16 hi = *reinterpret_cast<const v4i16*>(ks + 8 * st_);
+        const v4i16 lo = *reinterpret_cast<const v4i16*>(ks + HALF + 8 * st_);
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, qb[st_], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, qb[st_], s, 0, 0, 0);
+      }
+      t16_softmax_pv<D, true>(s, kvalid, scale_log2, sg.bias_log2,
+                              shared + b * T16Shared<D>::SLOT + 2 * HALF, st);
+    }
+    __syncthreads();  // the slots are rewritten by the next chunk
+  }
+}
+
 // F32: some segment has a float32 table (without it the float32 path, and its
 // registers, are not compiled in)
 template <bool O_BF16, int D, bool F32>
 __global__ __launch_bounds__(NW * 64) void attn_t16_kernel(T16Args a) {
   constexpr int CPL = D / 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NW * T16Lds<D>::BYTES];
+  // per-wave areas; with float32 segments also the shared area, which they alias
+  // (the shared segments are done, behind a barrier, before any per-wave area is used)
+  constexpr int SMEM = (F32 && T16Shared<D>::BYTES > NW * T16Lds<D>::BYTES) ? T16Shared<D>::BYTES
+                                                                            : NW * T16Lds<D>::BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t tile = (int64_t)blockIdx.x * NW + wave;
-  if (tile >= a.tiles) return;  // waves are independent: no barrier follows
+  // with a.share the tile count is a multiple of NW, so no wave of a workgroup that
+  // meets a barrier leaves here
+  if (tile >= a.tiles) return;
   uint8_t* lds = smem + wave * T16Lds<D>::BYTES;
   const int64_t t = tile % a.lists;
   const int64_t bh = tile / a.lists;
@@ -273,9 +361,23 @@ __global__ __launch_bounds__(NW * 64) void attn_t16_kernel(T16Args a) {
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) st.o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // float32 segments shared by the workgroup's tiles first (every wave takes part:
+  // a.share guarantees that the workgroup holds NW tiles of one (batch, head))
+  if constexpr (F32) {
+    if (a.share) {
+      for (int si = 0; si < a.n_seg; ++si) {
+        const T16Seg& sg = a.seg[si];
+        if (sg.bf16 || sg.shift < 2 || sg.count == 0 || sg.len == 0) continue;
+        const int32_t* lst = sg.idx + ((b * a.heads_q + h) * sg.rows + (t >> sg.shift)) * sg.stride;
+        t16_shared_segment<D>(a.scale_log2, sg, lst, (b * a.heads_kv + hk) * sg.len, qb, smem, st);
+      }
+    }
+  }
+
   for (int si = 0; si < a.n_seg; ++si) {
     const T16Seg& sg = a.seg[si];
     if (sg.count == 0 || sg.len == 0) continue;
+    if (F32 && a.share && !sg.bf16 && sg.shift >= 2) continue;  // done above
     const int32_t* lst = sg.idx + ((b * a.heads_q + h) * sg.rows + (t >> sg.shift)) * sg.stride;
     const int64_t head_row = (b * a.heads_kv + hk) * sg.len;
     if (!F32 || sg.bf16)
@@ -352,6 +454,7 @@ hipError_t launch_attn_t16(const basa_attn_desc* d, const void* q, void* o, int 
   a.heads_kv = (int)d->heads_kv;
   a.group = (int)(d->heads_q / d->heads_kv);
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
+  a.share = d->lists % NW == 0;
   if (a.tiles == 0) return hipSuccess;
   bool f32 = false;
   for (int i = 0; i < a.n_seg; ++i) f32 = f32 || !a.seg[i].bf16;

@@ -269,6 +269,29 @@ def test_attn_mfma_batch2_gqa(basa):
     assert el <= LSE_TOL, el
 
 
+@pytest.mark.parametrize("tokens,heads", [(2048, 2), (65536, 1)])
+def test_attn_mfma_all_blocks_is_dense_attention(basa, tokens, heads):
+    # keeping every key block is dense bidirectional attention (BA-Att section 2,
+    # Eq. 1), checked against the oracle's dense attention; at 65536 tokens the
+    # list has 512 entries, the largest the 64K-token shape can have
+    note(f"attn mfma: all {tokens // 128} blocks kept == dense attention, {heads} head(s)")
+    g = np.random.Generator(np.random.PCG64(30))
+    x = wl.make_dlm(31, heads=heads, tokens=tokens, head_dim=128)
+    nb = tokens // 128
+    idx = np.broadcast_to(np.arange(nb, dtype=np.int32), (1, heads, nb, nb)).copy()
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, 1 / math.sqrt(128),
+                      torch.float32)
+    if tokens > 4096:  # sampled query rows (the oracle's dense attention is O(L^2))
+        rows = np.sort(g.choice(tokens, 256, replace=False))
+        ro, rl = orc.dense_attention(x["q"][:, :, rows], x["k"], x["v"], 1 / math.sqrt(128))
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    else:
+        ro, rl = orc.dense_attention(x["q"], x["k"], x["v"], 1 / math.sqrt(128))
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    assert eo <= O_TOL, eo
+    assert el <= LSE_TOL, el
+
+
 def test_attn_mfma_dlm16k_sampled_and_deterministic(basa):
     note("attn mfma dlm16k: oracle lists, 48 sampled tiles, repeat-run bitwise")
     w = wl.WORKLOADS["dlm16k"]
