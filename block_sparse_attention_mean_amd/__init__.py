@@ -22,7 +22,7 @@ SELECT_BLOCKS, SELECT_CHANGE = 0, 1
 STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE",
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
-EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_attn",
+EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
            "basa_merge")
 
 
@@ -40,6 +40,7 @@ class SelectDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int64), ("scale", ctypes.c_double),
         ("q_rows", ctypes.c_void_p), ("parent", ctypes.c_void_p),
         ("parent_k", ctypes.c_int32), ("fanout", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -79,6 +80,8 @@ def _load() -> ctypes.CDLL:
     lib.basa_pool.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i32, vp]
     lib.basa_select.restype = i32
     lib.basa_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
+    lib.basa_select_workspace.restype = i32
+    lib.basa_select_workspace.argtypes = [ctypes.POINTER(SelectDesc), ctypes.POINTER(i64)]
     lib.basa_attn.restype = i32
     lib.basa_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, i32, vp, vp]
     lib.basa_merge.restype = i32
@@ -130,13 +133,7 @@ def basa_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None
                                       _ptr(mean_cols), _ptr(mean_copy), copy_dt, _stream()))
 
 
-def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
-                mode: int = SELECT_BLOCKS, scale: float = 1.0, heads_kv: int | None = None,
-                keys: int | None = None, q_rows: torch.Tensor | None = None,
-                parent: torch.Tensor | None = None, fanout: int = 1) -> None:
-    """BLOCKS: q [B,Hq,Lq,d] float64 means, k [B,Hkv,d,keys] float64 transposed means,
-    idx [B,Hq,rows,topk] int32.  CHANGE: q, k [B,H,T,d] current/previous queries,
-    idx [B,topk] int32."""
+def _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout):
     b, hq, lq, d = q.shape
     desc = SelectDesc()
     desc.mode = mode
@@ -155,8 +152,35 @@ def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, 
     desc.parent = _ptr(parent)
     desc.parent_k = parent.shape[-1] if parent is not None else 0
     desc.fanout = fanout
+    return desc
+
+
+def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
+                mode: int = SELECT_BLOCKS, scale: float = 1.0, heads_kv: int | None = None,
+                keys: int | None = None, q_rows: torch.Tensor | None = None,
+                parent: torch.Tensor | None = None, fanout: int = 1,
+                workspace: torch.Tensor | None = None) -> None:
+    """BLOCKS: q [B,Hq,Lq,d] float64 means, k [B,Hkv,d,keys] float64 transposed means,
+    idx [B,Hq,rows,topk] int32.  CHANGE: q, k [B,H,T,d] current/previous queries,
+    idx [B,topk] int32.  workspace: optional device scratch (uint8), see
+    basa_select_workspace."""
+    desc = _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout)
+    if workspace is not None:
+        desc.workspace = _ptr(workspace)
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
     _check("basa_select", lib.basa_select(ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q),
                                           _ptr(idx), _stream()))
+
+
+def basa_select_workspace(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
+                          mode: int = SELECT_BLOCKS, heads_kv: int | None = None,
+                          keys: int | None = None, q_rows: torch.Tensor | None = None,
+                          parent: torch.Tensor | None = None, fanout: int = 1) -> int:
+    """Bytes of workspace basa_select can use for this request (0: none)."""
+    desc = _select_desc(q, k, idx, topk, mode, 1.0, heads_kv, keys, q_rows, parent, fanout)
+    out = ctypes.c_int64(0)
+    _check("basa_select_workspace", lib.basa_select_workspace(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
 
 
 def kv_segment(idx: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, count: int | None = None,
@@ -222,6 +246,6 @@ def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b:
                                         _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
 
 
-__all__ = ["basa_pool", "basa_select", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
+__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE"]

@@ -98,6 +98,16 @@ int basa_select(const basa_select_desc* d, const void* q, const void* k, int dty
   }
 }
 
+int basa_select_workspace(const basa_select_desc* d, int64_t* bytes) {
+  try {
+    if (!d || !bytes) return BASA_E_NULLPTR;
+    *bytes = basa::select_workspace_bytes(d);
+    return BASA_OK;
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int o_dtype,
               float* lse, void* stream) {
   try {

@@ -35,6 +35,15 @@ struct SelArgs {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// A wave-uniform element of read-only input through the constant address space,
+// so it is fetched with a scalar load.  (A vector load would share the in-order
+// vector-memory counter with the key means streamed into LDS, and waiting for
+// it would wait for them.)
+typedef __attribute__((address_space(4))) const double const_f64;
+__device__ __forceinline__ double uniform_ld(const double* p) {
+  return *(const_f64*)p;
+}
+
 __device__ __forceinline__ uint64_t readfirstlane64(uint64_t x) {
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
   const uint32_t h = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
@@ -481,7 +490,7 @@ __device__ __forceinline__ void sel_chunk(const double* const* qp, int c0, doubl
     for (int j = 0; j < KPL; ++j) kv[j] = kc[cc * KPL * 64 + lane + 64 * j];
 #pragma unroll
     for (int i = 0; i < SEL_RW; ++i) {
-      const double qv = qp[i][c0 + cc];
+      const double qv = uniform_ld(qp[i] + c0 + cc);
 #pragma unroll
       for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
     }
@@ -553,6 +562,172 @@ __global__ __launch_bounds__(256, 2) void select_lds_kernel(SelArgs a, int64_t g
       if (sel[j]) out[base + popc64(m & below)] = lane + 64 * j;
       base += popc64(m);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide rows in two passes (workspace given; more than 1024 candidates, no
+// parent list, top-k <= 256).  The candidates are cut into parts of PART keys.
+// Pass 1: a workgroup takes one part for up to 4*PRW rows that read the same key
+// head (the rows of the query heads of one group, head-major), streams the
+// part's transposed means through LDS in 8-channel chunks (as the LDS-staged
+// kernel does), and writes each row's top-k of the part, in ascending key
+// order, to the workspace (empty slots: candidate -1).  Pass 2: one wave per
+// row takes the top-k of the parts' survivors, which are in ascending key
+// order part after part.  A key in the row's top-k is in its part's top-k
+// under the same order, so the result equals the one-pass selection.
+// ---------------------------------------------------------------------------
+constexpr int PART = 512;        // keys per part (KPL 8)
+constexpr int PRW = 2;           // rows per wave in pass 1
+constexpr int PMAX_K = 256;      // largest top-k of the two-pass path
+
+__host__ __device__ inline int64_t part_count(int64_t n_cand) { return (n_cand + PART - 1) / PART; }
+
+// chunk of 8 channels x PART keys of one part into LDS buffer P: channel row
+// c0+i lands at 4 KB * i; a lane whose key pair lies past the candidates reads
+// the last pair of the channel row instead (never used)
+template <int P>
+__device__ __forceinline__ void part_dma(const double* kt, int c0, int k0, int64_t keys, int n_cand) {
+  uint8_t* dst = P ? s_sel1 : s_sel0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int kp = k0 + (wave * 1024 + lane * 16) / 8;  // first key of this lane's pair
+  kp = kp + 1 < n_cand ? kp : ((n_cand - 2) & ~1);
+#pragma unroll
+  for (int i = 0; i < SEL_CH; ++i)
+    __builtin_amdgcn_global_load_lds(kt + (int64_t)(c0 + i) * keys + kp,
+                                     (lds_void*)(dst + i * 4096 + wave * 1024), 16, 0, 0);
+}
+
+template <int P>
+__device__ __forceinline__ void part_chunk(const double* const* qp, int c0, double (*acc)[PART / 64]) {
+  constexpr int KPL = PART / 64;
+  const double* kc = reinterpret_cast<const double*>(P ? s_sel1 : s_sel0);
+  const int lane = threadIdx.x & 63;
+#pragma unroll 2
+  for (int cc = 0; cc < SEL_CH; ++cc) {
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) kv[j] = kc[cc * PART + lane + 64 * j];
+#pragma unroll
+    for (int i = 0; i < PRW; ++i) {
+      const double qv = uniform_ld(qp[i] + c0 + cc);
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void select_part_kernel(SelArgs a, int n_parts, int64_t groups,
+                                                            uint64_t* __restrict__ ws_key,
+                                                            int32_t* __restrict__ ws_cand) {
+  constexpr int KPL = PART / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (b, kv head, part, row group), row group fastest: neighbouring workgroups
+  // read the same part of the same key head
+  const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+  const int64_t rg = unit % groups;
+  const int p = (int)((unit / groups) % n_parts);
+  const int hk = (int)((unit / (groups * n_parts)) % a.heads_kv);
+  const int b = (int)(unit / (groups * n_parts * a.heads_kv));
+  const int64_t rows_kv = (int64_t)a.group * a.rows;  // rows that read key head hk
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+  const int k0 = p * PART;
+
+  // this wave's rows: kv-head row r -> query head hk*group + r/rows, row r%rows
+  const double* qp[PRW];
+  int64_t orow[PRW];
+#pragma unroll
+  for (int i = 0; i < PRW; ++i) {
+    const int64_t r = rg * 4 * PRW + wave * PRW + i;
+    const int64_t rr = r < rows_kv ? r : 0;
+    const int h = hk * a.group + (int)(rr / a.rows);
+    const int64_t row = rr % a.rows;
+    int64_t qr = row;
+    if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + row];
+    if (qr < 0 || qr >= a.q_len) qr = 0;  // a row map entry outside q reads row 0
+    qr = __builtin_amdgcn_readfirstlane((int)qr);
+    qp[i] = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
+    orow[i] = r < rows_kv ? (((int64_t)b * a.heads_q + h) * a.rows + row) : -1;
+  }
+  double acc[PRW][KPL];
+#pragma unroll
+  for (int i = 0; i < PRW; ++i)
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
+
+  const int n_chunk = a.d / SEL_CH;  // even (checked at launch)
+  part_dma<0>(kt, 0, k0, a.keys, a.n_cand);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int c = 0; c < n_chunk; c += 2) {
+    part_dma<1>(kt, (c + 1) * SEL_CH, k0, a.keys, a.n_cand);
+    part_chunk<0>(qp, c * SEL_CH, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (c + 2 < n_chunk) part_dma<0>(kt, (c + 2) * SEL_CH, k0, a.keys, a.n_cand);
+    part_chunk<1>(qp, (c + 1) * SEL_CH, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < PRW; ++i) {
+    if (orow[i] < 0) continue;
+    uint64_t key[KPL];
+    bool valid[KPL], sel[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      valid[j] = k0 + lane + 64 * j < a.n_cand;
+      key[j] = valid[j] ? ordered_key(acc[i][j]) : 0ull;
+    }
+    wave_topk<KPL>(key, valid, a.topk, below, sel);
+    uint64_t* wk = ws_key + (orow[i] * n_parts + p) * a.topk;
+    int32_t* wc = ws_cand + (orow[i] * n_parts + p) * a.topk;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const uint64_t m = __ballot(sel[j]);
+      if (sel[j]) {
+        const int pos = base + popc64(m & below);
+        wk[pos] = key[j];
+        wc[pos] = k0 + lane + 64 * j;
+      }
+      base += popc64(m);
+    }
+    for (int e = base + lane; e < a.topk; e += 64) wc[e] = -1;  // fewer than k candidates
+  }
+}
+
+template <int KPL2>
+__global__ __launch_bounds__(256) void select_merge_kernel(SelArgs a, int n_parts, int64_t n_rows,
+                                                           const uint64_t* __restrict__ ws_key,
+                                                           const int32_t* __restrict__ ws_cand) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, h, row) flattened
+  if (r >= n_rows) return;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int n_e = n_parts * a.topk;
+  uint64_t key[KPL2];
+  bool valid[KPL2], sel[KPL2];
+  int cand[KPL2];
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const int e = lane + 64 * j;
+    cand[j] = e < n_e ? ws_cand[r * n_e + e] : -1;
+    valid[j] = cand[j] >= 0;
+    key[j] = valid[j] ? ws_key[r * n_e + e] : 0ull;
+  }
+  wave_topk<KPL2>(key, valid, a.topk, below, sel);
+  int32_t* out = a.idx + r * a.topk;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const uint64_t m = __ballot(sel[j]);
+    if (sel[j]) out[base + popc64(m & below)] = cand[j];
+    base += popc64(m);
   }
 }
 
@@ -645,6 +820,16 @@ __global__ __launch_bounds__(256) void select_change_kernel(const T* __restrict_
 
 }  // namespace
 
+int64_t select_workspace_bytes(const basa_select_desc* d) {
+  // (an even key count keeps the 16-byte loads of key pairs aligned)
+  if (d->mode != BASA_SELECT_BLOCKS || d->parent || d->keys <= 1024 || d->keys > 4096 ||
+      d->keys % 2 != 0 || d->topk > PMAX_K || d->topk < 1 || d->batch < 1 || d->rows < 1 ||
+      d->heads_q < 1 || d->head_dim % (2 * SEL_CH) != 0)
+    return 0;
+  const int64_t n_rows = d->batch * d->heads_q * d->rows;
+  return n_rows * part_count(d->keys) * d->topk * (int64_t)(sizeof(uint64_t) + sizeof(int32_t));
+}
+
 hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, const double* kt,
                                 int32_t* idx, hipStream_t s) {
   SelArgs a;
@@ -686,6 +871,26 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   }
   if (kpl <= 8) return one_row ? launch_kr<8, 1>(a, d->batch, s) : launch_kr<8, 4>(a, d->batch, s);
   if (kpl <= 16) return launch_kr<16, 1>(a, d->batch, s);
+  const int64_t ws_need = select_workspace_bytes(d);
+  if (ws_need > 0 && d->workspace && d->workspace_bytes >= ws_need &&
+      (reinterpret_cast<uintptr_t>(d->workspace) & 7) == 0) {
+    // two passes: parts of PART keys, then the merge
+    const int n_parts = (int)part_count(a.n_cand);
+    const int64_t n_rows = d->batch * a.heads_q * a.rows;
+    uint64_t* ws_key = static_cast<uint64_t*>(d->workspace);
+    int32_t* ws_cand = reinterpret_cast<int32_t*>(ws_key + n_rows * n_parts * a.topk);
+    const int64_t groups = ((int64_t)a.group * a.rows + 4 * PRW - 1) / (4 * PRW);
+    dim3 g1((unsigned)(groups * n_parts * a.heads_kv * d->batch), 1);
+    select_part_kernel<<<g1, 256, 0, s>>>(a, n_parts, groups, ws_key, ws_cand);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 g2((unsigned)((n_rows + 3) / 4), 1);
+    if (n_parts * a.topk <= 16 * 64)
+      select_merge_kernel<16><<<g2, 256, 0, s>>>(a, n_parts, n_rows, ws_key, ws_cand);
+    else
+      select_merge_kernel<32><<<g2, 256, 0, s>>>(a, n_parts, n_rows, ws_key, ws_cand);
+    return hipGetLastError();
+  }
   if (a.topk <= WIDE_MAX_K) {  // a workgroup per row, four quarters of at most 1024
     dim3 grid((unsigned)a.rows, (unsigned)a.heads_q, (unsigned)d->batch);
     select_wide_kernel<16><<<grid, 256, 0, s>>>(a);

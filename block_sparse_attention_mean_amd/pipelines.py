@@ -21,7 +21,7 @@ import math
 import torch
 
 from . import (SELECT_BLOCKS, SELECT_CHANGE, basa_attn, basa_merge, basa_pool, basa_select,
-               kv_segment)
+               basa_select_workspace, kv_segment)
 
 
 def _empty(*shape, dtype, like):
@@ -191,6 +191,9 @@ class LosaStep:
         self.lse_in = _empty(b, hq, t, dtype=torch.float32, like=q_cur)
         self.o = torch.empty_like(q_cur)
         self.lse = _empty(b, hq, t, dtype=torch.float32, like=q_cur)
+        # scratch of the prefix selection (lets it run in two passes over 512-key parts)
+        n_ws = basa_select_workspace(self.q64, self.kbt, self.sel, topk, q_rows=self.active)
+        self.ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q_cur.device) if n_ws else None
 
     def prepare(self):
         basa_pool(self.k_prefix, self.block, mean_cols=self.kbt)
@@ -200,7 +203,7 @@ class LosaStep:
         basa_select(self.q_cur, self.q_prev, self.active, self.n_active, mode=SELECT_CHANGE)
         basa_pool(self.q_cur, 1, mean_rows=self.q64)
         basa_select(self.q64, self.kbt, self.sel, self.topk, scale=self.scale,
-                    q_rows=self.active)
+                    q_rows=self.active, workspace=self.ws)
         basa_attn(self.q_cur, kv_segment(self.sel, self.k_prefix, self.v_prefix), self.cache_o,
                   self.cache_lse, tile_q=1, block_k=self.block, scale=self.scale,
                   q_rows=self.active)

@@ -106,6 +106,13 @@ typedef struct basa_select_desc {
   const int32_t* parent;
   int32_t parent_k;
   int32_t fanout;
+  /* optional device scratch, owned by the caller (NULL: none).  Rows with
+     more than 1024 candidates and no parent list are selected in two passes
+     when it holds at least basa_select_workspace() bytes (otherwise in one,
+     slower, pass; the result is the same).  The call overwrites it; calls
+     that overlap in time must not share it. */
+  void* workspace;
+  int64_t workspace_bytes;
 } basa_select_desc;
 /* (parent entries outside [0, keys/fanout) are treated as no candidate.) */
 
@@ -138,6 +145,17 @@ typedef struct basa_select_desc {
  */
 int basa_select(const basa_select_desc* desc, const void* q, const void* k, int dtype,
                 int32_t* idx, void* stream);
+
+/*
+ * basa_select_workspace - bytes of workspace that lets basa_select take the
+ * two-pass path for this request (0: the request never uses one).  Reads
+ * only the sizes in desc (mode, batch, heads_q, rows, keys, topk, parent).
+ * The two passes compute the same selection as one (BA-Att section 3.1): the
+ * candidates are split into parts of 512 keys, each part keeps its own top-k,
+ * and the top-k of the union of the parts' top-k is the row's top-k.
+ * Errors: BASA_E_NULLPTR for a NULL desc or bytes.
+ */
+int basa_select_workspace(const basa_select_desc* desc, int64_t* bytes);
 
 /* One source of keys for basa_attn.  The key list of query tile t is the
  * concatenation, over the descriptor's segments, of `count` entries of row

@@ -82,6 +82,24 @@ def select(desc, q=FAKE, k=FAKE, dt=basa.F64, idx=FAKE):
     return basa.lib.basa_select(ctypes.byref(desc), q, k, dt, idx, None)
 
 
+def test_select_workspace_size():
+    # host-only: bytes of scratch for the two-pass path over > 1024 candidates
+    def ws(**kw):
+        n = ctypes.c_int64(-1)
+        assert basa.lib.basa_select_workspace(ctypes.byref(sel_desc(**kw)), ctypes.byref(n)) == OK
+        return n.value
+    assert ws() == 0                                        # 16 keys: one pass
+    assert ws(keys=1024, topk=64) == 0
+    # 2 x 5 rows, 4096 keys = 8 parts of 512, top-128: (key, candidate) = 12 bytes each
+    assert ws(keys=4096, topk=128, rows=5, q_rows=FAKE) == 2 * 5 * 8 * 128 * 12
+    assert ws(keys=3000, topk=10) == 2 * 16 * 6 * 10 * 12  # a partial last part
+    assert ws(keys=4096, topk=300) == 0                     # top-k beyond the two-pass path
+    assert ws(keys=4096, topk=8, parent=FAKE, parent_k=2, fanout=4) == 0
+    assert ws(keys=4096, topk=8, mode=basa.SELECT_CHANGE) == 0
+    assert basa.lib.basa_select_workspace(None, ctypes.byref(ctypes.c_int64())) == NULLPTR
+    assert basa.lib.basa_select_workspace(ctypes.byref(sel_desc()), None) == NULLPTR
+
+
 def test_select_validation():
     assert basa.lib.basa_select(None, FAKE, FAKE, basa.F64, FAKE, None) == NULLPTR
     assert select(sel_desc(topk=0)) == SHAPE

@@ -127,18 +127,27 @@ def test_select_exact_ties_go_to_lower_index(basa):
     assert np.array_equal(got[0, 0, 0], np.arange(150))
 
 
-@pytest.mark.parametrize("ties", [False, True])
-def test_select_gqa_row_map_and_wide_rows(basa, ties):
-    note(f"select GQA 8/2 heads, row map, 4096 keys (top-128), ties={ties}")
+@pytest.mark.parametrize("ties,keys,workspace", [(False, 4096, False), (True, 4096, False),
+                                                  (False, 4096, True), (True, 4096, True),
+                                                  (False, 3000, True)])
+def test_select_gqa_row_map_and_wide_rows(basa, ties, keys, workspace):
+    # more than 1024 candidates: one pass without a workspace, two passes (parts of
+    # 512 keys, then a merge) with one; the result must not depend on the path
+    note(f"select GQA 8/2 heads, row map, {keys} keys (top-128), ties={ties}, workspace={workspace}")
     g = np.random.Generator(np.random.PCG64(16))
     qf = g.standard_normal((1, 8, 16, 128))
-    kbar = g.standard_normal((1, 2, 4096, 128))
-    if ties:  # 64 distinct key rows repeated: equal scores across the four quarters
-        kbar = np.tile(kbar[:, :, :64], (1, 1, 64, 1))
+    kbar = g.standard_normal((1, 2, keys, 128))
+    if ties:  # 64 distinct key rows repeated: equal scores across quarters and parts
+        kbar = np.tile(kbar[:, :, :64], (1, 1, keys // 64, 1))
     rows = np.array([[1, 4, 7, 10, 13]], dtype=np.int32)
     idx = torch.empty(1, 8, 5, 128, dtype=torch.int32, device="cuda")
-    basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 128,
-                     scale=1 / math.sqrt(128), q_rows=dev(rows))
+    qt, kt = dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2)))
+    ws = None
+    if workspace:
+        n = basa.basa_select_workspace(qt, kt, idx, 128, q_rows=dev(rows))
+        assert n == 8 * 5 * ((keys + 511) // 512) * 128 * 12
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    basa.basa_select(qt, kt, idx, 128, scale=1 / math.sqrt(128), q_rows=dev(rows), workspace=ws)
     torch.cuda.synchronize()
     ref = orc.topk_ascending(orc.block_logits(qf[:, :, rows[0]], kbar, 1 / math.sqrt(128)), 128)
     assert np.array_equal(host(idx), ref)
