@@ -21,8 +21,7 @@
 // Software pipeline.  Stage i issues the MFMAs of S(i+1) and, in the same
 // instruction stream, the exponentials of S(i) (exp2, row sum, bf16
 // packing), so the vector ALU works while the matrix core does; then the
-// MFMAs of O += P(i) V(i) next to the row max of S(i+1), which fixes the max
-// (and the rescale of O) before stage i+1 starts.
+// MFMAs of O += P(i) V(i).
 //
 // Key permutation.  The 32x32 accumulator puts row rho of S^T in register
 // r = 4*(rho/8) + rho%4 of lane-half (rho/4)%2.  Loading key kappa into MFMA
@@ -43,10 +42,11 @@
 //   V: rows of 256 bytes, chunk c of row r at chunk (c + 4 (r & 3)) & 15, so
 //      the four rows of one transposing read cover all banks once.
 //
-// Softmax: log2 domain with the scale folded in; the running max is only
-// raised when a stage's max exceeds it by more than 8 (a factor 256), so the
-// O rescale is usually skipped; O/l and LSE = m + log2(l) do not depend on the
-// choice of m.
+// Softmax: log2 domain with the scale folded in.  m starts at the first
+// stage's row max and is not tracked per stage: the exponentials are taken
+// against it and only when a lane's share of a stage's row sum exceeds 2^32
+// (a logit above m + 27) is the row max taken, m raised, O rescaled and the
+// stage redone.  O/l and LSE = m + log2(l) do not depend on the choice of m.
 //
 // Workgroup numbering: dispatch hands workgroups to the 8 XCDs round-robin.
 // Tiles are numbered so that in every round of 8 x 64 resident workgroups all
@@ -66,7 +66,7 @@ constexpr int NT = 256;                       // threads per workgroup (4 waves)
 constexpr int SBYTES = SK * D * 2;            // 16 KB per K or V stage
 constexpr int MAX_KEPT = 1024;                // list slots staged in LDS (the last holds the count)
 constexpr int RESIDENT_PER_XCD = 64;          // two workgroups per CU, 32 CUs per XCD
-constexpr float kLazy = 8.0f;                 // log2 of the allowed growth before a rescale
+constexpr float kBound = 4294967296.0f;       // 2^32: largest lane share of a row sum taken as is
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -160,26 +160,19 @@ __device__ __forceinline__ void qk(const Walk& w, const bf16x8* qf, f32x16* s) {
   }
 }
 
-// Row max of one stage's logits (log2 units): raises m lazily and rescales l;
-// returns the factor the output accumulators still have to be scaled by.
-__device__ __forceinline__ float max_stage(const f32x16* s, float scale_log2, float& m, float& l) {
+// Row max of the first stage's logits (log2 units), the starting m.
+__device__ __forceinline__ float max_stage(const f32x16* s, float scale_log2) {
   float mx = s[0][0];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-  const float m_new = mx > m + kLazy ? fmaxf(m, mx) : m;
-  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-  m = m_new;
-  l *= alpha;
-  return alpha;
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
 }
 
-// P = exp2(scale*S - m) as bf16 MFMA operands; adds the row sum to l.
-__device__ __forceinline__ void exp_stage(const f32x16* s, float scale_log2, float m, float& l,
-                                          bf16x8* pf) {
+// P = exp2(scale*S - m) as bf16 MFMA operands; returns the lane's share of the row sum.
+__device__ __forceinline__ float exp_stage(const f32x16* s, float scale_log2, float m, bf16x8* pf) {
   float psum = 0.f;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -191,7 +184,38 @@ __device__ __forceinline__ void exp_stage(const f32x16* s, float scale_log2, flo
         psum += p;
         pf[2 * st + cc][j] = (__bf16)p;
       }
-  l += psum;
+  return psum;
+}
+
+// The exponentials of a stage are taken against the running max m, which is
+// only raised when they grow too large: a lane share above 2^32 means some
+// logit exceeds m by more than 27 (log2 units).  Then the row max of the
+// stage raises m (for both lanes of the row), O and l are rescaled and the
+// stage is exponentiated again.  Values below the bound keep O, l and P far
+// inside the float range.
+__device__ __forceinline__ float exp_checked(const f32x16* s, float scale_log2, float& m, float& l,
+                                             f32x16* oacc, bf16x8* pf) {
+  float psum = exp_stage(s, scale_log2, m, pf);
+  if (__ballot(!(psum <= kBound)) != 0) {  // rare, wave-uniform
+    float mx = s[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+    const auto sw =
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+    psum = exp_stage(s, scale_log2, m, pf);
+  }
+  return psum;
 }
 
 // O^T += V^T P^T over the 64 keys in V buffer P, 16 keys at a time
@@ -212,42 +236,25 @@ __device__ __forceinline__ void pv(const Walk& w, const bf16x8* pf, f32x16* oacc
   }
 }
 
-__device__ __forceinline__ void rescale(f32x16* oacc, float alpha) {
-  if (__ballot(alpha != 1.0f) != 0) {  // some row raised its max (wave-uniform branch)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-  }
-}
-
-// One stage i with buffer parity P = i & 1.  On entry S(i) is in s_cur with m
-// already raised for it (alpha: the pending rescale of O), K(i+1) sits in K
-// buffer P^1 and V(i) in V buffer P; S(i+1) goes to s_next.  NEXT: stage i+1
-// exists.
+// One stage i with buffer parity P = i & 1.  On entry S(i) is in s_cur,
+// K(i+1) sits in K buffer P^1 and V(i) in V buffer P; S(i+1) goes to s_next.
+// NEXT: stage i+1 exists.
 template <int P, bool NEXT>
 __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, const f32x16* s_cur,
                                       f32x16* s_next, f32x16* oacc, float& m, float& l,
-                                      float& alpha, float scale_log2) {
+                                      float scale_log2) {
   if (NEXT) {
     // K(i) and V(i-1) were consumed by stage i-1; past the end, K(n-1) is fetched again
     dma_k<P>(w, min(i + 2, w.n_stage - 1));
     dma_v<P ^ 1>(w, i + 1);
   }
-  rescale(oacc, alpha);
   bf16x8 pf[4];
+  if (NEXT) qk<P ^ 1>(w, qf, s_next);  // S(i+1) on the matrix core while P(i) is formed
+  l += exp_checked(s_cur, scale_log2, m, l, oacc, pf);
+  pv<P>(w, pf, oacc);
   if (NEXT) {
-    // S(i+1) on the matrix core while the vector unit exponentiates S(i)
-    qk<P ^ 1>(w, qf, s_next);
-    exp_stage(s_cur, scale_log2, m, l, pf);
-    // O += P(i) V(i) while the row max of S(i+1) is taken
-    pv<P>(w, pf, oacc);
-    alpha = max_stage(s_next, scale_log2, m, l);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of stage i+1 have landed
     __syncthreads();                     // ... and everyone's; buffers of stage i are free
-  } else {
-    exp_stage(s_cur, scale_log2, m, l, pf);
-    pv<P>(w, pf, oacc);
   }
 }
 
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[u][r] = 0.f;
-  float m = -INFINITY;  // running row max of scale*log2(e)*logit (lazily raised)
+  float m = -INFINITY;  // reference max of scale*log2(e)*logit (raised only on overflow risk)
   float l = 0.f;        // this lane's share of the running row sum
 
   if (w.n_stage > 0) {
@@ -333,15 +340,15 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
     __syncthreads();
     f32x16 s_a[2], s_b[2];  // logits of even / odd stages
     qk<0>(w, qf, s_a);
-    float alpha = max_stage(s_a, a.scale_log2, m, l);
+    m = max_stage(s_a, a.scale_log2);
     // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
     int i = 0;
     for (; i + 2 < w.n_stage; i += 2) {
-      stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, alpha, a.scale_log2);
-      stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, m, l, alpha, a.scale_log2);
+      stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, a.scale_log2);
+      stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, m, l, a.scale_log2);
     }
-    stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, alpha, a.scale_log2);
-    stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, m, l, alpha, a.scale_log2);
+    stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, a.scale_log2);
+    stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, m, l, a.scale_log2);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no load into this workgroup's LDS outlives it
   }
 

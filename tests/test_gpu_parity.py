@@ -301,6 +301,33 @@ def test_attn_mfma_all_blocks_is_dense_attention(basa, tokens, heads):
     assert el <= LSE_TOL, el
 
 
+@pytest.mark.parametrize("rising", [True, False])
+def test_attn_mfma_rising_logits_raise_the_reference_max(basa, rising):
+    # key blocks scaled by growing factors: walking a list in ascending order meets
+    # logits far above the first block's max, so the kernel must raise its reference
+    # max, rescale O and redo stages (several times per row); the descending case
+    # starts at the largest logits and never has to
+    note(f"attn mfma: key blocks scaled 1..20, rising={rising}")
+    g = np.random.Generator(np.random.PCG64(33))
+    heads, tokens, nb = 2, 2048, 16
+    factor = np.array([1, 1, 2, 3, 5, 8, 12, 16, 20, 4, 1, 6, 2, 9, 14, 18], dtype=np.float32)
+    if not rising:
+        factor = factor[::-1].copy()
+    q = wl.f32_to_bf16(g.standard_normal((1, heads, tokens, 128)).astype(np.float32))
+    kf = g.standard_normal((1, heads, tokens, 128)).astype(np.float32)
+    k = wl.f32_to_bf16(kf * np.repeat(factor, 128)[None, None, :, None])
+    v = wl.f32_to_bf16(g.standard_normal((1, heads, tokens, 128)).astype(np.float32))
+    idx = np.sort(np.stack([np.stack([g.choice(nb, 7, replace=False) for _ in range(nb)])
+                            for _ in range(heads)]), axis=-1)[None].astype(np.int32)
+    idx[0, 0, 3] = np.arange(9, dtype=np.int32)[:7]       # a row walking factors 1, 1, 2, .., 12
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 128, 128, 1 / math.sqrt(128), torch.float32)
+    ro, rl = orc.sparse_attention(q, k, v, idx, 128, 128, 1 / math.sqrt(128))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    assert eo <= O_TOL, eo
+    assert el <= LSE_TOL, el
+
+
 def test_attn_mfma_dlm16k_sampled_and_deterministic(basa):
     note("attn mfma dlm16k: oracle lists, 48 sampled tiles, repeat-run bitwise")
     w = wl.WORKLOADS["dlm16k"]
