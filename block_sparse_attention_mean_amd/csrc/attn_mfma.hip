@@ -341,6 +341,7 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
     f32x16 s_a[2], s_b[2];  // logits of even / odd stages
     qk<0>(w, qf, s_a);
     m = max_stage(s_a, a.scale_log2);
+    __syncthreads();  // every wave has read K(0) before stage 0 refills its buffer with K(2)
     // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
     int i = 0;
     for (; i + 2 < w.n_stage; i += 2) {
