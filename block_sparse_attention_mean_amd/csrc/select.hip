@@ -450,41 +450,47 @@ __global__ __launch_bounds__(256) void select_split_kernel(SelArgs a, int64_t gr
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged rows (exactly 64*KPL keys, no parent list): a workgroup per 32
-// rows of one head, eight per wave.  The key means are read once per
-// workgroup: chunks of 8 channels x all keys go from global memory straight
-// into LDS (double-buffered, one barrier per chunk), and the four waves take
-// their key values from there; every key value feeds eight rows.
+// LDS-staged rows (exactly 64*KPL keys, no parent list): a workgroup per 16
+// rows of one head, four per wave, four workgroups per CU.  The key means are
+// read once per workgroup: chunks of 4 channels x all keys go from global
+// memory straight into LDS (double-buffered, 16 KB each, one barrier per
+// chunk), and the four waves take their key values from there; every key
+// value feeds four rows.  (Eight rows per wave, 8-channel chunks and two
+// workgroups per CU measured 11% slower: fewer waves to hide the latency.)
+// The two-pass kernel below keeps the 8-channel chunks (SEL_CH).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int SEL_CH = 8;  // channels per staged chunk
 
-template <int KPL>
-struct SelStage {
-  static constexpr int BYTES = SEL_CH * KPL * 64 * 8;
-};
-__shared__ __attribute__((aligned(16))) uint8_t s_sel0[SelStage<8>::BYTES];
-__shared__ __attribute__((aligned(16))) uint8_t s_sel1[SelStage<8>::BYTES];
+constexpr int SEL_BYTES = SEL_CH * 8 * 64 * 8;  // 8 channels x 512 keys of float64
+__shared__ __attribute__((aligned(16))) uint8_t s_sel0[SEL_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_sel1[SEL_BYTES];
 
-template <int KPL, int P>
-__device__ __forceinline__ void sel_dma(const double* src) {
-  uint8_t* dst = P ? s_sel1 : s_sel0;
+constexpr int LDS_CH = 4;                        // channels per staged chunk (LDS-staged rows)
+constexpr int LDS_BYTES = LDS_CH * 8 * 64 * 8;   // 4 channels x 512 keys of float64
+__shared__ __attribute__((aligned(16))) uint8_t s_lds0[LDS_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t s_lds1[LDS_BYTES];
+
+constexpr int SEL_RW = 4;  // rows per wave (LDS-staged rows)
+
+// chunk of LDS_CH channels x 512 keys into buffer P (16 B per lane per copy)
+template <int P>
+__device__ __forceinline__ void lds_dma(const double* src) {
+  uint8_t* dst = P ? s_lds1 : s_lds0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-  for (int i = 0; i < SelStage<KPL>::BYTES / 4096; ++i)
+  for (int i = 0; i < LDS_BYTES / 4096; ++i)
     __builtin_amdgcn_global_load_lds(src + (i * 4096 + tid * 16) / 8,
                                      (lds_void*)(dst + i * 4096 + wave * 1024), 16, 0, 0);
 }
 
-constexpr int SEL_RW = 8;  // rows per wave
-
 template <int KPL, int P>
 __device__ __forceinline__ void sel_chunk(const double* const* qp, int c0, double (*acc)[KPL]) {
-  const double* kc = reinterpret_cast<const double*>(P ? s_sel1 : s_sel0);
+  const double* kc = reinterpret_cast<const double*>(P ? s_lds1 : s_lds0);
   const int lane = threadIdx.x & 63;
 #pragma unroll 2
-  for (int cc = 0; cc < SEL_CH; ++cc) {
+  for (int cc = 0; cc < LDS_CH; ++cc) {
     double kv[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) kv[j] = kc[cc * KPL * 64 + lane + 64 * j];
@@ -498,7 +504,7 @@ __device__ __forceinline__ void sel_chunk(const double* const* qp, int c0, doubl
 }
 
 template <int KPL>
-__global__ __launch_bounds__(256, 2) void select_lds_kernel(SelArgs a, int64_t groups) {
+__global__ __launch_bounds__(256, 4) void select_lds_kernel(SelArgs a, int64_t groups) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
@@ -524,19 +530,19 @@ __global__ __launch_bounds__(256, 2) void select_lds_kernel(SelArgs a, int64_t g
 #pragma unroll
     for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
 
-  // chunks of SEL_CH channels; head_dim / SEL_CH is even (checked at launch)
-  const int n_chunk = a.d / SEL_CH;
-  const int64_t chunk_elems = (int64_t)SEL_CH * a.keys;
-  sel_dma<KPL, 0>(kt);
+  // chunks of LDS_CH channels; head_dim / LDS_CH is even (checked at launch)
+  const int n_chunk = a.d / LDS_CH;
+  const int64_t chunk_elems = (int64_t)LDS_CH * a.keys;
+  lds_dma<0>(kt);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int k = 0; k < n_chunk; k += 2) {
-    sel_dma<KPL, 1>(kt + (k + 1) * chunk_elems);
-    sel_chunk<KPL, 0>(qp, k * SEL_CH, acc);
+    lds_dma<1>(kt + (k + 1) * chunk_elems);
+    sel_chunk<KPL, 0>(qp, k * LDS_CH, acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (k + 2 < n_chunk) sel_dma<KPL, 0>(kt + (k + 2) * chunk_elems);
-    sel_chunk<KPL, 1>(qp, (k + 1) * SEL_CH, acc);
+    if (k + 2 < n_chunk) lds_dma<0>(kt + (k + 2) * chunk_elems);
+    sel_chunk<KPL, 1>(qp, (k + 1) * LDS_CH, acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
@@ -857,7 +863,7 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   if (kpl <= 1) return one_row ? launch_kr<1, 1>(a, d->batch, s) : launch_kr<1, 4>(a, d->batch, s);
   if (kpl <= 2) return one_row ? launch_kr<2, 1>(a, d->batch, s) : launch_kr<2, 4>(a, d->batch, s);
   if (kpl <= 4) return one_row ? launch_kr<4, 1>(a, d->batch, s) : launch_kr<4, 4>(a, d->batch, s);
-  if (!d->parent && a.keys == 512 && a.d % (2 * SEL_CH) == 0) {  // LDS-staged key means
+  if (!d->parent && a.keys == 512 && a.d % (2 * LDS_CH) == 0) {  // LDS-staged key means
     const int64_t groups = (a.rows + 4 * SEL_RW - 1) / (4 * SEL_RW);
     dim3 grid((unsigned)(groups * a.heads_q * d->batch), 1);
     select_lds_kernel<8><<<grid, 256, 0, s>>>(a, groups);
