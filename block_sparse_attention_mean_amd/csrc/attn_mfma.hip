@@ -42,11 +42,14 @@
 //   V: rows of 256 bytes, chunk c of row r at chunk (c + 4 (r & 3)) & 15, so
 //      the four rows of one transposing read cover all banks once.
 //
-// Softmax: log2 domain with the scale folded in.  m starts at the first
-// stage's row max and is not tracked per stage: the exponentials are taken
-// against it and only when a lane's share of a stage's row sum exceeds 2^32
-// (a logit above m + 27) is the row max taken, m raised, O rescaled and the
-// stage redone.  O/l and LSE = m + log2(l) do not depend on the choice of m.
+// Softmax: log2 domain with the scale folded in.  The exponentials of every
+// stage are taken against a fixed reference m, the first stage's row max; no
+// row max is tracked per stage and O is never rescaled inside the walk.  When
+// a lane's share of a stage's row sum exceeds 2^32 (a logit above m + 27),
+// the stage's row max is recorded and, after the walk, the whole workgroup
+// walks the tile again from that larger m (rare: the logits of a tile rise
+// that far above its first stage only for adversarial inputs).  O/l and
+// LSE = m + log2(l) do not depend on the choice of m.
 //
 // Workgroup numbering: dispatch hands workgroups to the 8 XCDs round-robin.
 // Tiles are numbered so that in every round of 8 x 64 resident workgroups all
@@ -77,6 +80,7 @@ __shared__ __attribute__((aligned(16))) uint8_t s_k1[SBYTES];
 __shared__ __attribute__((aligned(16))) uint8_t s_v0[SBYTES];
 __shared__ __attribute__((aligned(16))) uint8_t s_v1[SBYTES];
 __shared__ int32_t s_lst[MAX_KEPT];
+__shared__ int32_t s_flag;  // set when the walk needs a second pass
 
 struct MfmaArgs {
   const uint16_t* q;
@@ -187,36 +191,17 @@ __device__ __forceinline__ float exp_stage(const f32x16* s, float scale_log2, fl
   return psum;
 }
 
-// The exponentials of a stage are taken against the running max m, which is
-// only raised when they grow too large: a lane share above 2^32 means some
-// logit exceeds m by more than 27 (log2 units).  Then the row max of the
-// stage raises m (for both lanes of the row), O and l are rescaled and the
-// stage is exponentiated again.  Values below the bound keep O, l and P far
-// inside the float range.
-__device__ __forceinline__ float exp_checked(const f32x16* s, float scale_log2, float& m, float& l,
-                                             f32x16* oacc, bf16x8* pf) {
-  float psum = exp_stage(s, scale_log2, m, pf);
-  if (__ballot(!(psum <= kBound)) != 0) {  // rare, wave-uniform
-    float mx = s[0][0];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-    const auto sw =
-        __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-    psum = exp_stage(s, scale_log2, m, pf);
-  }
-  return psum;
-}
+// Row state of the walk.  The exponentials are taken against a fixed
+// reference m (log2 units), the first stage's row max.  A lane share of a
+// stage's row sum above 2^32 means a logit exceeds m by more than 27: the
+// stage's row max is then recorded in m_seen and the walk is marked for a
+// second pass, which starts from m = m_seen and cannot overflow (every logit
+// of the tile is at most m_seen + 32).  Values below the bound keep O, l and
+// P far inside the float range.
+struct Rows {
+  float m, m_seen, l;
+  bool over;
+};
 
 // O^T += V^T P^T over the 64 keys in V buffer P, 16 keys at a time
 template <int P>
@@ -241,8 +226,7 @@ __device__ __forceinline__ void pv(const Walk& w, const bf16x8* pf, f32x16* oacc
 // NEXT: stage i+1 exists.
 template <int P, bool NEXT>
 __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, const f32x16* s_cur,
-                                      f32x16* s_next, f32x16* oacc, float& m, float& l,
-                                      float scale_log2) {
+                                      f32x16* s_next, f32x16* oacc, Rows& r, float scale_log2) {
   if (NEXT) {
     // K(i) and V(i-1) were consumed by stage i-1; past the end, K(n-1) is fetched again
     dma_k<P>(w, min(i + 2, w.n_stage - 1));
@@ -250,8 +234,13 @@ __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, co
   }
   bf16x8 pf[4];
   if (NEXT) qk<P ^ 1>(w, qf, s_next);  // S(i+1) on the matrix core while P(i) is formed
-  l += exp_checked(s_cur, scale_log2, m, l, oacc, pf);
+  const float psum = exp_stage(s_cur, scale_log2, r.m, pf);
+  r.l += psum;
   pv<P>(w, pf, oacc);
+  if (__ballot(!(psum <= kBound)) != 0) {  // rare, wave-uniform: the walk is redone
+    r.over = true;
+    r.m_seen = fmaxf(r.m_seen, max_stage(s_cur, scale_log2));
+  }
   if (NEXT) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of stage i+1 have landed
     __syncthreads();                     // ... and everyone's; buffers of stage i are free
@@ -317,41 +306,55 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
       if (ok) s_lst[n + __popcll(msk & below)] = blk;
       n += __popcll(msk);
     }
-    if (lane == 0) s_lst[MAX_KEPT - 1] = n;  // kept < MAX_KEPT, so the count slot is never an entry
+    if (lane == 0) {
+      s_lst[MAX_KEPT - 1] = n;  // kept < MAX_KEPT, so the count slot is never an entry
+      s_flag = 0;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // Q loads settled (compiler-visible vmcnt(0))
   __syncthreads();
   w.n_stage = 2 * s_lst[MAX_KEPT - 1];
 
   f32x16 oacc[4];
+  Rows r;
+  r.over = false;
+  r.m_seen = -INFINITY;
+  // At most two passes over the kept blocks: the second only when a logit
+  // exceeded the first stage's row max by more than 27 (log2 units).
+  for (int pass = 0;; ++pass) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[u][r] = 0.f;
-  float m = -INFINITY;  // reference max of scale*log2(e)*logit (raised only on overflow risk)
-  float l = 0.f;        // this lane's share of the running row sum
-
-  if (w.n_stage > 0) {
-    // prologue: K(0), K(1), V(0); then S(0)
-    dma_k<0>(w, 0);
-    dma_k<1>(w, 1);
-    dma_v<0>(w, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    f32x16 s_a[2], s_b[2];  // logits of even / odd stages
-    qk<0>(w, qf, s_a);
-    m = max_stage(s_a, a.scale_log2);
-    __syncthreads();  // every wave has read K(0) before stage 0 refills its buffer with K(2)
-    // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
-    int i = 0;
-    for (; i + 2 < w.n_stage; i += 2) {
-      stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, a.scale_log2);
-      stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, m, l, a.scale_log2);
+      for (int e = 0; e < 16; ++e) oacc[u][e] = 0.f;
+    r.l = 0.f;
+    r.m = -INFINITY;
+    if (w.n_stage > 0) {
+      // prologue: K(0), K(1), V(0); then S(0)
+      dma_k<0>(w, 0);
+      dma_k<1>(w, 1);
+      dma_v<0>(w, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      f32x16 s_a[2], s_b[2];  // logits of even / odd stages
+      qk<0>(w, qf, s_a);
+      r.m = pass == 0 ? max_stage(s_a, a.scale_log2) : r.m_seen;
+      r.m_seen = r.m;
+      __syncthreads();  // every wave has read K(0) before stage 0 refills its buffer with K(2)
+      // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
+      int i = 0;
+      for (; i + 2 < w.n_stage; i += 2) {
+        stage<0, true>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
+        stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
+      }
+      stage<0, true>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
+      stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
     }
-    stage<0, true>(w, i, qf, s_a, s_b, oacc, m, l, a.scale_log2);
-    stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, m, l, a.scale_log2);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // no load into this workgroup's LDS outlives it
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no load into this workgroup's LDS outlives the walk
+    if (pass == 0 && r.over) s_flag = 1;
+    __syncthreads();  // every wave is done with the stage buffers; the flag is settled
+    if (pass != 0 || s_flag == 0) break;  // workgroup-uniform
   }
+  const float m = r.m, l = r.l;
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
   const float l_tot = l + __shfl_xor(l, 32);
