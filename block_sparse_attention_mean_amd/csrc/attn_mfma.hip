@@ -68,6 +68,7 @@ constexpr int SK = 64;                        // keys per stage
 constexpr int NT = 256;                       // threads per workgroup (4 waves)
 constexpr int SBYTES = SK * D * 2;            // 16 KB per K or V stage
 constexpr int MAX_KEPT = 1024;                // list slots staged in LDS (the last holds the count)
+constexpr int REG_KEPT = 128;                 // lists up to this long are also held in two VGPRs
 constexpr int RESIDENT_PER_XCD = 64;          // two workgroups per CU, 32 CUs per XCD
 constexpr float kBound = 4294967296.0f;       // 2^32: largest lane share of a row sum taken as is
 
@@ -116,26 +117,32 @@ struct Walk {
   const uint16_t* vbase;
   int koff[4], voff[4];    // element offsets of this lane's DMA chunks within a stage
   int vrd[4];              // byte offsets of this lane's V^T operand reads (per 32-channel group)
+  int lst0, lst1;          // short lists: entry e in lane e % 64 of lst0 (e < 64) or lst1
   int wave, krow_l, hi, n_stage;
 };
 
-// first element of stage j (64 keys) of the head's K or V
-__device__ __forceinline__ int64_t stage_elem(int j) {
-  return ((int64_t)s_lst[j >> 1] * BK + (j & 1) * SK) * D;
+// first element of stage j (64 keys) of the head's K or V.  A short list is
+// read from the VGPRs (wave-uniform lane select, no LDS access); a long one
+// from LDS.
+template <bool REG>
+__device__ __forceinline__ int64_t stage_elem(const Walk& w, int j) {
+  const int e = j >> 1;
+  const int blk = REG ? __builtin_amdgcn_readlane(e < 64 ? w.lst0 : w.lst1, e & 63) : s_lst[e];
+  return ((int64_t)blk * BK + (j & 1) * SK) * D;
 }
 
-template <int P>
+template <int P, bool REG>
 __device__ __forceinline__ void dma_k(const Walk& w, int j) {
-  const uint16_t* g = w.kbase + stage_elem(j);
+  const uint16_t* g = w.kbase + stage_elem<REG>(w, j);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds(g + w.koff[i], (lds_void*)(kbuf<P>() + (16 * w.wave + 4 * i) * 256),
                                      16, 0, 0);
 }
 
-template <int P>
+template <int P, bool REG>
 __device__ __forceinline__ void dma_v(const Walk& w, int j) {
-  const uint16_t* g = w.vbase + stage_elem(j);
+  const uint16_t* g = w.vbase + stage_elem<REG>(w, j);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds(g + w.voff[i], (lds_void*)(vbuf<P>() + (16 * w.wave + 4 * i) * 256),
@@ -224,13 +231,13 @@ __device__ __forceinline__ void pv(const Walk& w, const bf16x8* pf, f32x16* oacc
 // One stage i with buffer parity P = i & 1.  On entry S(i) is in s_cur,
 // K(i+1) sits in K buffer P^1 and V(i) in V buffer P; S(i+1) goes to s_next.
 // NEXT: stage i+1 exists.
-template <int P, bool NEXT>
+template <int P, bool NEXT, bool REG>
 __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, const f32x16* s_cur,
                                       f32x16* s_next, f32x16* oacc, Rows& r, float scale_log2) {
   if (NEXT) {
     // K(i) and V(i-1) were consumed by stage i-1; past the end, K(n-1) is fetched again
-    dma_k<P>(w, min(i + 2, w.n_stage - 1));
-    dma_v<P ^ 1>(w, i + 1);
+    dma_k<P, REG>(w, min(i + 2, w.n_stage - 1));
+    dma_v<P ^ 1, REG>(w, i + 1);
   }
   bf16x8 pf[4];
   if (NEXT) qk<P ^ 1>(w, qf, s_next);  // S(i+1) on the matrix core while P(i) is formed
@@ -247,7 +254,7 @@ __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, co
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool REG>
 __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t tile = tile_of(blockIdx.x, a.tiles);
   const int64_t t = tile % a.lists;
@@ -314,6 +321,10 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // Q loads settled (compiler-visible vmcnt(0))
   __syncthreads();
   w.n_stage = 2 * s_lst[MAX_KEPT - 1];
+  if (REG) {
+    w.lst0 = s_lst[lane];
+    w.lst1 = s_lst[64 + lane];
+  }
 
   f32x16 oacc[4];
   Rows r;
@@ -330,9 +341,9 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
     r.m = -INFINITY;
     if (w.n_stage > 0) {
       // prologue: K(0), K(1), V(0); then S(0)
-      dma_k<0>(w, 0);
-      dma_k<1>(w, 1);
-      dma_v<0>(w, 0);
+      dma_k<0, REG>(w, 0);
+      dma_k<1, REG>(w, 1);
+      dma_v<0, REG>(w, 0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       f32x16 s_a[2], s_b[2];  // logits of even / odd stages
@@ -343,11 +354,11 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
       // n_stage is even: stages go in pairs (even, odd); the last pair ends the walk
       int i = 0;
       for (; i + 2 < w.n_stage; i += 2) {
-        stage<0, true>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
-        stage<1, true>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
+        stage<0, true, REG>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
+        stage<1, true, REG>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
       }
-      stage<0, true>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
-      stage<1, false>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
+      stage<0, true, REG>(w, i, qf, s_a, s_b, oacc, r, a.scale_log2);
+      stage<1, false, REG>(w, i + 1, qf, s_b, s_a, oacc, r, a.scale_log2);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no load into this workgroup's LDS outlives the walk
     if (pass == 0 && r.over) s_flag = 1;
@@ -414,10 +425,18 @@ hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
   if (a.tiles == 0) return hipSuccess;
   dim3 grid((unsigned)a.tiles);
-  if (o_dtype == BASA_BF16)
-    attn_mfma_kernel<true><<<grid, NT, 0, s>>>(a);
-  else
-    attn_mfma_kernel<false><<<grid, NT, 0, s>>>(a);
+  const bool reg = g.count <= REG_KEPT;
+  if (o_dtype == BASA_BF16) {
+    if (reg)
+      attn_mfma_kernel<true, true><<<grid, NT, 0, s>>>(a);
+    else
+      attn_mfma_kernel<true, false><<<grid, NT, 0, s>>>(a);
+  } else {
+    if (reg)
+      attn_mfma_kernel<false, true><<<grid, NT, 0, s>>>(a);
+    else
+      attn_mfma_kernel<false, false><<<grid, NT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
