@@ -12,9 +12,34 @@
 namespace basa {
 namespace {
 
+// The partials are read once and the result written once: nontemporal
+// accesses keep them from displacing other data in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename TIN> struct Load8NT;
+template <> struct Load8NT<float> {
+  static __device__ __forceinline__ void load(const float* p, float* out) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[i] = __uint_as_float(a[i]);
+      out[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+};
+template <> struct Load8NT<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* out) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_bits_to_f32(a[i] & 0xFFFFu);
+      out[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+    }
+  }
+};
 template <typename TIN>
 __device__ __forceinline__ void load8(const void* p, int64_t i, float* out) {
-  Vec8<TIN>::load(static_cast<const TIN*>(p) + i, out);
+  Load8NT<TIN>::load(static_cast<const TIN*>(p) + i, out);
 }
 
 template <typename TIN, typename TOUT>
@@ -49,11 +74,14 @@ __global__ __launch_bounds__(256) void merge_kernel(int64_t rows, int d, const v
     pk.y = (uint32_t)f32_to_bf16_bits(r[2]) | ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
     pk.z = (uint32_t)f32_to_bf16_bits(r[4]) | ((uint32_t)f32_to_bf16_bits(r[5]) << 16);
     pk.w = (uint32_t)f32_to_bf16_bits(r[6]) | ((uint32_t)f32_to_bf16_bits(r[7]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(o) + row * d + c) = pk;
+    __builtin_nontemporal_store(u32x4{pk.x, pk.y, pk.z, pk.w},
+                                reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o) + row * d + c));
   } else {
     float* op = static_cast<float*>(o) + row * d + c;
-    *reinterpret_cast<float4*>(op) = make_float4(r[0], r[1], r[2], r[3]);
-    *reinterpret_cast<float4*>(op + 4) = make_float4(r[4], r[5], r[6], r[7]);
+    __builtin_nontemporal_store(u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]), __float_as_uint(r[2]),
+                                      __float_as_uint(r[3])}, reinterpret_cast<u32x4*>(op));
+    __builtin_nontemporal_store(u32x4{__float_as_uint(r[4]), __float_as_uint(r[5]), __float_as_uint(r[6]),
+                                      __float_as_uint(r[7])}, reinterpret_cast<u32x4*>(op + 4));
   }
   if (c == 0) lse[row] = lm;
 }
