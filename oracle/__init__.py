@@ -22,6 +22,12 @@ pages it cites:
 
 Nothing here is blocked, fused or reordered beyond what those definitions
 state.  Library primitives used as steps: numpy matmul, sort, exp, log.
+
+basa_oracle_ref.cpp is a second, independent fp64 reference of the BA-Att
+steps (pooling, block logits, top-k, block-sparse and merged attention) in
+plain C++ loops, compiled with g++ into liboracle_ref.so and reached through
+oracle.cref.  Both references are pinned to the same independent facts and
+checked against each other.
 """
 from .basa_oracle import *  # noqa: F401,F403
 from .basa_oracle import __all__  # noqa: F401

@@ -519,3 +519,34 @@ def test_merge_in_place(basa):
     torch.cuda.synchronize()
     ro, rl = orc.merge(oa, la, ob, lb)
     assert max_err(host(toa), ro) <= 1e-5 and max_err(host(tla), rl) <= 1e-5
+
+
+# ------------------------------------------------------------- C++ reference
+
+def test_ba_path_matches_cpp_reference(basa):
+    """Selection, block-sparse attention and a two-part merge on a DLM-shaped
+    case, every row against the fp64 C++ reference (oracle/basa_oracle_ref.cpp)."""
+    import oracle.cref as cref
+    note("BA path H2 L4096 d128 top-8 against the C++ reference")
+    x = wl.make_dlm(41, heads=2, tokens=4096, head_dim=128)
+    block, topk, scale = 128, 8, 1 / math.sqrt(128)
+    ref_idx = cref.topk_ascending(cref.block_logits(cref.pool_mean(x["q"], block),
+                                                    cref.pool_mean(x["k"], block), scale), topk)
+    assert np.array_equal(gpu_select(basa, x["q"], x["k"], block, topk, scale), ref_idx)
+    o, lse = run_attn(basa, x["q"], [(ref_idx, x["k"], x["v"], {})], 128, 128, scale, torch.bfloat16)
+    ro, rl = cref.sparse_attention(x["q"], x["k"], x["v"], ref_idx, 128, 128, scale)
+    assert max_err(o, ro) <= O_TOL
+    assert max_err(lse, rl) <= LSE_TOL
+    # halves of every list as float32 partials, merged on the GPU and by the reference
+    oa, la = run_attn(basa, x["q"], [(ref_idx, x["k"], x["v"], {"count": 4})], 128, 128, scale,
+                      torch.float32)
+    ob, lb = run_attn(basa, x["q"], [(ref_idx, x["k"], x["v"], {"offset": 4, "count": 4})], 128, 128,
+                      scale, torch.float32)
+    om = torch.empty(o.shape, dtype=torch.bfloat16, device="cuda")
+    lm = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
+    f32 = lambda a: dev(a.astype(np.float32))  # the partials were float32 (read back widened)
+    basa.basa_merge(f32(oa), f32(la), f32(ob), f32(lb), om, lm)
+    torch.cuda.synchronize()
+    rmo, rml = cref.merge(oa, la, ob, lb)
+    assert max_err(host(om), rmo) <= O_TOL and max_err(host(lm), rml) <= 1e-5
+    assert max_err(host(om), ro) <= O_TOL and max_err(host(lm), rl) <= LSE_TOL
