@@ -1,8 +1,9 @@
 // Block mean pooling (BA-Att section 3.1: block representatives are the means
 // of their rows; the log-linear README pools level by level the same way).
 //
-// One workgroup per (outer, block).  Each thread reads 8 consecutive channels
-// of a row with one 16/32/64-byte load, walking down the block in steps of
+// One workgroup per (outer, pair of consecutive blocks), or per block when the
+// block count is odd.  Each thread reads 8 consecutive channels of a row with
+// one 16/32/64-byte load, walking down each block in steps of
 // (256 / (head_dim/8)) rows, and keeps float64 partial sums.  The partial sums
 // of the row groups are combined through LDS in a fixed order, so the result
 // does not depend on scheduling.  For bf16 inputs and power-of-two blocks the
@@ -16,35 +17,50 @@ namespace {
 // data in the caches (measured ~6% faster on the 64K-token workload).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Load8<T>: one row's 8 channels.  load() issues the read, add() widens the
+// values and adds them to the float64 partial sums; the main loop issues all
+// of a step's reads before the first add so that they are in flight together.
 template <typename T> struct Load8;
 template <> struct Load8<uint16_t> {
-  static __device__ __forceinline__ void add(const uint16_t* p, double* acc) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  struct Raw { u32x4 a; };
+  static __device__ __forceinline__ Raw load(const uint16_t* p) {
+    return {__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))};
+  }
+  static __device__ __forceinline__ void add(const Raw& r, double* acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += (double)bf16_bits_to_f32(a[i] & 0xFFFFu);
-      acc[2 * i + 1] += (double)bf16_bits_to_f32(a[i] >> 16);
+      acc[2 * i] += (double)bf16_bits_to_f32(r.a[i] & 0xFFFFu);
+      acc[2 * i + 1] += (double)bf16_bits_to_f32(r.a[i] >> 16);
     }
   }
 };
 template <> struct Load8<float> {
-  static __device__ __forceinline__ void add(const float* p, double* acc) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+  struct Raw { u32x4 a, b; };
+  static __device__ __forceinline__ Raw load(const float* p) {
+    return {__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)),
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4))};
+  }
+  static __device__ __forceinline__ void add(const Raw& r, double* acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[i] += (double)__uint_as_float(a[i]);
-      acc[4 + i] += (double)__uint_as_float(b[i]);
+      acc[i] += (double)__uint_as_float(r.a[i]);
+      acc[4 + i] += (double)__uint_as_float(r.b[i]);
     }
   }
 };
 template <> struct Load8<double> {
-  static __device__ __forceinline__ void add(const double* p, double* acc) {
+  struct Raw { double2 a[4]; };
+  static __device__ __forceinline__ Raw load(const double* p) {
+    Raw r;
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      double2 a = *reinterpret_cast<const double2*>(p + i);
-      acc[i] += a.x;
-      acc[i + 1] += a.y;
+    for (int i = 0; i < 4; ++i) r.a[i] = *reinterpret_cast<const double2*>(p + 2 * i);
+    return r;
+  }
+  static __device__ __forceinline__ void add(const Raw& r, double* acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += r.a[i].x;
+      acc[2 * i + 1] += r.a[i].y;
     }
   }
 };
@@ -58,44 +74,62 @@ __device__ __forceinline__ int64_t xcd_major(int64_t id, int64_t n) {
   return (id % 8) * per + id / 8;
 }
 
-template <typename T>
+template <typename T, int BPW>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int64_t len, int d,
                                                    int block, int64_t nb, int64_t n_wg,
                                                    double* __restrict__ mean_rows,
                                                    double* __restrict__ mean_cols,
                                                    void* __restrict__ mean_copy, int copy_dtype) {
-  __shared__ double red[2048];  // [row groups][head_dim], row groups * head_dim == 2048
+  __shared__ double red[BPW][2048];  // [block of the workgroup][row groups][head_dim]
   const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
   if (lin >= n_wg) return;
   const int64_t wg = xcd_major(lin, n_wg);
-  const int64_t o = wg / nb;
-  const int64_t g = wg - o * nb;
+  const int64_t per_outer = nb / BPW;
+  const int64_t o = wg / per_outer;
+  const int64_t g0 = (wg - o * per_outer) * BPW;
   const int cols8 = d >> 3;
   const int groups = 256 / cols8;
   const int t = threadIdx.x;
   const int rg = t / cols8;
   const int c8 = t - rg * cols8;
-  const T* src = x + (o * len + g * (int64_t)block) * d + c8 * 8;
-  double acc[8];
+  double acc[BPW][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int s2 = 0; s2 < BPW; ++s2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[s2][i] = 0.0;
   if (rg < groups) {
+    const T* src = x + (o * len + g0 * (int64_t)block) * d + c8 * 8;
     int r = rg;
-    // eight independent rows in flight per iteration
+    // eight rows of each of the BPW blocks in flight per step
     for (; r + 7 * groups < block; r += 8 * groups) {
+      typename Load8<T>::Raw raw[BPW][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Load8<T>::add(src + (int64_t)(r + u * groups) * d, acc);
+      for (int s2 = 0; s2 < BPW; ++s2)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) raw[s2][u] = Load8<T>::load(src + ((int64_t)s2 * block + r + u * groups) * d);
+#pragma unroll
+      for (int s2 = 0; s2 < BPW; ++s2)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Load8<T>::add(raw[s2][u], acc[s2]);
     }
-    for (; r < block; r += groups) Load8<T>::add(src + (int64_t)r * d, acc);
+    for (; r < block; r += groups) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[rg * d + c8 * 8 + i] = acc[i];
+      for (int s2 = 0; s2 < BPW; ++s2)
+        Load8<T>::add(Load8<T>::load(src + ((int64_t)s2 * block + r) * d), acc[s2]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < BPW; ++s2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[s2][rg * d + c8 * 8 + i] = acc[s2][i];
   }
   __syncthreads();
   const int used = groups < block ? groups : block;
   const double inv_n = (double)block;
-  for (int c = t; c < d; c += 256) {
+  for (int e = t; e < BPW * d; e += 256) {
+    const int s2 = e / d, c = e - s2 * d;
+    const int64_t g = g0 + s2;
     double s = 0.0;
-    for (int r = 0; r < used; ++r) s += red[r * d + c];
+    for (int r = 0; r < used; ++r) s += red[s2][r * d + c];
     const double mean = s / inv_n;
     if (mean_rows) mean_rows[(o * nb + g) * d + c] = mean;
     if (mean_cols) mean_cols[(o * d + c) * nb + g] = mean;
@@ -108,33 +142,46 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int6
   }
 }
 
+template <typename T>
+hipError_t launch_typed(const T* x, int64_t outer, int64_t len, int d, int block, double* mean_rows,
+                        double* mean_cols, void* mean_copy, int copy_dtype, hipStream_t s) {
+  const int64_t nb = len / block;
+  // two consecutive blocks per workgroup when the count allows (bf16 and
+  // float32 inputs): twice the loads in flight per thread (the 64K pooling:
+  // 194 -> 178 us); four blocks need 64 KB of LDS per workgroup and measured
+  // no better than one
+  const bool two = nb % 2 == 0 && sizeof(T) < 8;
+  const int64_t n_wg = outer * (two ? nb / 2 : nb);
+  const int64_t gx = n_wg < 65536 ? n_wg : 65536;
+  const int64_t gy = (n_wg + gx - 1) / gx;
+  dim3 grid((unsigned)gx, (unsigned)gy);
+  if (two)
+    pool_kernel<T, 2><<<grid, 256, 0, s>>>(x, len, d, block, nb, n_wg, mean_rows, mean_cols, mean_copy,
+                                           copy_dtype);
+  else
+    pool_kernel<T, 1><<<grid, 256, 0, s>>>(x, len, d, block, nb, n_wg, mean_rows, mean_cols, mean_copy,
+                                           copy_dtype);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                        int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
                        int copy_dtype, hipStream_t s) {
-  const int64_t nb = len / block;
-  const int64_t n_wg = outer * nb;
-  if (n_wg == 0) return hipSuccess;
-  const int64_t gx = n_wg < 65536 ? n_wg : 65536;
-  const int64_t gy = (n_wg + gx - 1) / gx;
-  dim3 grid((unsigned)gx, (unsigned)gy);
+  if (outer * (len / block) == 0) return hipSuccess;
   const int d = (int)head_dim, b = (int)block;
   switch (x_dtype) {
     case BASA_BF16:
-      pool_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), len, d, b, nb,
-                                                  n_wg, mean_rows, mean_cols, mean_copy, copy_dtype);
-      break;
+      return launch_typed(static_cast<const uint16_t*>(x), outer, len, d, b, mean_rows, mean_cols,
+                          mean_copy, copy_dtype, s);
     case BASA_F32:
-      pool_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), len, d, b, nb, n_wg,
-                                               mean_rows, mean_cols, mean_copy, copy_dtype);
-      break;
+      return launch_typed(static_cast<const float*>(x), outer, len, d, b, mean_rows, mean_cols,
+                          mean_copy, copy_dtype, s);
     default:
-      pool_kernel<double><<<grid, 256, 0, s>>>(static_cast<const double*>(x), len, d, b, nb, n_wg,
-                                                mean_rows, mean_cols, mean_copy, copy_dtype);
-      break;
+      return launch_typed(static_cast<const double*>(x), outer, len, d, b, mean_rows, mean_cols,
+                          mean_copy, copy_dtype, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace basa

@@ -521,6 +521,26 @@ def test_merge_in_place(basa):
     assert max_err(host(toa), ro) <= 1e-5 and max_err(host(tla), rl) <= 1e-5
 
 
+@pytest.mark.parametrize("kept", [128, 129, 130])
+def test_attn_mfma_list_length_boundary(basa, kept):
+    """Lists of up to 128 blocks are held in VGPRs, longer ones read from LDS:
+    both sides of the boundary, with repeated and unused entries."""
+    note(f"attn mfma: kept {kept} of 256 blocks, 1 head, L 32768")
+    x = wl.make_dlm(43, heads=1, tokens=32768, head_dim=128)
+    nb, scale = 256, 1 / math.sqrt(128)
+    g = np.random.Generator(np.random.PCG64(44 + kept))
+    idx = np.sort(g.integers(0, nb, (1, 1, nb, kept)), axis=-1).astype(np.int32)  # repeats allowed
+    idx[0, 0, 5, 0] = -1
+    idx[0, 0, 9, kept - 1] = nb + 1
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, scale, torch.bfloat16)
+    tiles = [0, 5, 9, 100, 255]
+    ro, rl = orc.sparse_attention(x["q"], x["k"], x["v"], np.where(idx >= nb, -1, idx), 128, 128, scale,
+                                  lists=[(0, 0, t) for t in tiles])
+    sel = ~np.isnan(rl)
+    assert max_err(o[sel], ro[sel]) <= O_TOL
+    assert max_err(lse[sel], rl[sel]) <= LSE_TOL
+
+
 # ------------------------------------------------------------- C++ reference
 
 def test_ba_path_matches_cpp_reference(basa):
