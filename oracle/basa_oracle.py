@@ -13,6 +13,7 @@ __all__ = [
     "as_f64", "pool_mean", "block_logits", "topk_ascending", "attend_rows",
     "sparse_attention", "dense_attention", "merge", "llsa_num_levels", "llsa_forward",
     "llsa_keys_per_query", "token_change", "active_tokens", "losa_step",
+    "norm_key", "norm_rank", "gather_rows", "scatter_rows", "ba_forward_ranked",
 ]
 
 
@@ -198,6 +199,73 @@ def merge(o_a, lse_a, o_b, lse_b):
     wa = np.where(empty, 0.0, np.exp(lse_a - lse_safe))[..., None]
     wb = np.where(empty, 0.0, np.exp(lse_b - lse_safe))[..., None]
     return wa * o_a + wb * o_b, lse
+
+
+# ---------------------------------------------------------------------------
+# BA-Att, section 3.3 (Eq. 9-10) and Algorithm 1 steps 1, 2 and 12:
+# norm-based ranking of the tokens before the blocks are formed
+# ---------------------------------------------------------------------------
+
+def norm_key(x) -> np.ndarray:
+    """Squared l2 norm of every token, float64: [..., L, d] -> [..., L].
+
+    BA-Att section 3.3, Eq. 9 scores a token by its l2 norm.  The square
+    orders the tokens the same way in exact arithmetic and needs no square
+    root (whose rounding could merge two distinct norms).  The channels are
+    added one after another, c = 0, 1, ..., d-1.  For bf16 inputs every square
+    and every partial sum is exact unless one token's squares span more than
+    about 2^37 in magnitude.
+    """
+    x = as_f64(x)
+    s = np.zeros(x.shape[:-1])
+    for c in range(x.shape[-1]):
+        s = s + x[..., c] * x[..., c]
+    return s
+
+
+def norm_rank(x) -> np.ndarray:
+    """The permutation of BA-Att Eq. 10, per sequence: int32 [..., L].
+
+    Position i of the ranked sequence holds token perm[i]; the norms are
+    non-decreasing along the ranked sequence.  Tokens with equal norms keep
+    their order (a stable sort: the pages do not say how ties go).  Every
+    leading index (batch, head) is ranked on its own, over the whole sequence
+    (Algorithm 1 mentions a "(windowed)" sort without giving a window).
+    """
+    return np.argsort(norm_key(x), axis=-1, kind="stable").astype(np.int32)
+
+
+def gather_rows(x, perm) -> np.ndarray:
+    """X'[..., i, :] = X[..., perm[i], :] (Algorithm 1 steps 1 and 2)."""
+    x = np.asarray(x)
+    return np.take_along_axis(x, np.asarray(perm, dtype=np.int64)[..., None], axis=-2)
+
+
+def scatter_rows(x, perm) -> np.ndarray:
+    """Out[..., perm[i], :] = X[..., i, :]: the inverse of gather_rows
+    (Algorithm 1 step 12 remaps the outputs to the original order by pi_q^-1)."""
+    x = np.asarray(x)
+    out = np.empty_like(x)
+    np.put_along_axis(out, np.asarray(perm, dtype=np.int64)[..., None], x, axis=-2)
+    return out
+
+
+def ba_forward_ranked(q, k, v, block: int, topk: int, scale: float):
+    """BA-Att Algorithm 1 with norm ranking and without covariance compensation
+    (beta = 0): rank Q by its token norms and K (with V) by theirs, pool, score
+    and select on the ranked sequences, attend there, and return O and LSE in
+    the original query order.  Returns (perm_q, perm_k, idx, O, LSE); idx
+    indexes ranked key blocks.
+    """
+    pq, pk = norm_rank(q), norm_rank(k)
+    qs = gather_rows(as_f64(q), pq)
+    ks = gather_rows(as_f64(k), pk)
+    vs = gather_rows(as_f64(v), pk)
+    idx = topk_ascending(block_logits(pool_mean(qs, block), pool_mean(ks, block), scale), topk)
+    o_s, lse_s = sparse_attention(qs, ks, vs, idx, block, block, scale)
+    o = scatter_rows(o_s, pq)
+    lse = scatter_rows(lse_s[..., None], pq)[..., 0]
+    return pq, pk, idx, o, lse
 
 
 # ---------------------------------------------------------------------------
