@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libbasa.so")
 
 F32, BF16, F64 = 0, 1, 2
 SELECT_BLOCKS, SELECT_CHANGE = 0, 1
+PERMUTE_GATHER, PERMUTE_SCATTER = 0, 1
 
 STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE",
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
-           "basa_merge")
+           "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute")
 
 
 class BasaError(RuntimeError):
@@ -86,6 +87,12 @@ def _load() -> ctypes.CDLL:
     lib.basa_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, i32, vp, vp]
     lib.basa_merge.restype = i32
     lib.basa_merge.argtypes = [i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp]
+    lib.basa_rank_workspace.restype = i32
+    lib.basa_rank_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
+    lib.basa_rank.restype = i32
+    lib.basa_rank.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp]
+    lib.basa_permute.restype = i32
+    lib.basa_permute.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp]
     return lib
 
 
@@ -246,6 +253,54 @@ def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b:
                                         _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
 
 
+def _outer_len(x: torch.Tensor, lead_dims: int) -> tuple[int, int]:
+    outer = 1
+    for s in x.shape[:lead_dims]:
+        outer *= s
+    return outer, x.shape[lead_dims]
+
+
+def basa_rank_workspace(outer: int, length: int) -> int:
+    """Bytes of device workspace basa_rank needs for `outer` sequences of `length` tokens."""
+    out = ctypes.c_int64(0)
+    _check("basa_rank_workspace", lib.basa_rank_workspace(outer, length, ctypes.byref(out)))
+    return out.value
+
+
+def basa_rank(x: torch.Tensor, perm: torch.Tensor, workspace: torch.Tensor | None = None) -> None:
+    """perm [..., L] int32 <- the order of x [..., L, d]'s tokens by non-decreasing l2 norm
+    (stable), per sequence.  workspace: uint8 device tensor of basa_rank_workspace bytes
+    (allocated here when not given)."""
+    if perm.dtype != torch.int32 or perm.shape != x.shape[:-1]:
+        raise TypeError("perm must be int32 with x's shape minus the channel dimension")
+    outer, length = _outer_len(x, x.dim() - 2)
+    need = basa_rank_workspace(outer, length)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("basa_rank", lib.basa_rank(_ptr(x), _dt(x), outer, length, x.shape[-1], _ptr(perm),
+                                      _ptr(workspace), workspace.numel(), _stream()))
+
+
+def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
+                 mode: int = PERMUTE_GATHER) -> None:
+    """Rows of x moved by perm [..., L]: GATHER out[i] = x[perm[i]], SCATTER out[perm[i]] = x[i].
+    x and out are [..., L, width] or, for width 1, [..., L] (e.g. an LSE)."""
+    if perm.dtype != torch.int32:
+        raise TypeError("perm must be int32")
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise TypeError("out must match x in shape and dtype")
+    if x.shape == perm.shape:
+        width = 1
+    elif x.shape[:-1] == perm.shape:
+        width = x.shape[-1]
+    else:
+        raise TypeError("perm must be x's shape, or x's shape minus the last dimension")
+    outer, length = _outer_len(perm, perm.dim() - 1)
+    _check("basa_permute", lib.basa_permute(_ptr(x), _dt(x), outer, length, width, _ptr(perm),
+                                            mode, _ptr(out), _stream()))
+
+
 __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
-           "SELECT_CHANGE"]
+           "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
+           "PERMUTE_SCATTER"]

@@ -1,6 +1,7 @@
 // C ABI of libbasa: host-side argument checks, then dispatch to the kernels.
 // Every check runs before any HIP call, so an invalid request enqueues nothing
 // and touches no device state.
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -167,6 +168,55 @@ int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse
     if (o == o_b && o_dtype != in_dtype) return BASA_E_UNSUPPORTED;
     return from_hip(basa::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, in_dtype, o,
                                        o_dtype, lse, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes) {
+  try {
+    if (!bytes) return BASA_E_NULLPTR;
+    if (outer < 0 || len < 0 || (len > 0 && outer > INT32_MAX / len)) return BASA_E_SHAPE;
+    *bytes = basa::rank_workspace_bytes(outer, len);
+    return BASA_OK;
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+              int32_t* perm, void* workspace, int64_t workspace_bytes, void* stream) {
+  try {
+    if (outer < 0 || len < 0 || (len > 0 && outer > INT32_MAX / len)) return BASA_E_SHAPE;
+    if (head_dim < 8 || head_dim > 512 || head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (x_dtype != BASA_F32 && x_dtype != BASA_BF16 && x_dtype != BASA_F64) return BASA_E_DTYPE;
+    if (outer * len == 0) return BASA_OK;
+    if (!x || !perm || !workspace) return BASA_E_NULLPTR;
+    if (!aligned16(x) || !aligned16(perm) || !aligned16(workspace)) return BASA_E_ALIGN;
+    if (workspace_bytes < basa::rank_workspace_bytes(outer, len)) return BASA_E_SHAPE;
+    return from_hip(basa::launch_rank(x, x_dtype, outer, len, head_dim, perm, workspace,
+                                      workspace_bytes, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_permute(const void* x, int dtype, int64_t outer, int64_t len, int64_t width,
+                 const int32_t* perm, int mode, void* out, void* stream) {
+  try {
+    if (outer < 0 || len < 0 || width < 1) return BASA_E_SHAPE;
+    if (dtype != BASA_F32 && dtype != BASA_BF16 && dtype != BASA_F64) return BASA_E_DTYPE;
+    if (mode != BASA_PERMUTE_GATHER && mode != BASA_PERMUTE_SCATTER) return BASA_E_UNSUPPORTED;
+    if (outer * len == 0) return BASA_OK;
+    if (!x || !perm || !out) return BASA_E_NULLPTR;
+    if (!aligned16(x) || !aligned16(perm) || !aligned16(out)) return BASA_E_ALIGN;
+    const int64_t esize = dtype == BASA_BF16 ? 2 : (dtype == BASA_F32 ? 4 : 8);
+    const int64_t row_bytes = width * esize;
+    const int64_t bytes = outer * len * row_bytes;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
+    if (xa < oa + (uintptr_t)bytes && oa < xa + (uintptr_t)bytes) return BASA_E_UNSUPPORTED;
+    return from_hip(basa::launch_permute(x, outer, len, row_bytes, perm, mode, out,
+                                         static_cast<hipStream_t>(stream)));
   } catch (...) {
     return BASA_E_LAUNCH;
   }

@@ -1,0 +1,180 @@
+// Norm-based token ranking and row permutation (BA-Att section 3.3, Eq. 9-10;
+// Algorithm 1 steps 1, 2 and 12).
+//
+// Ranking.  Every token gets a sort key: its squared l2 norm in float64, the
+// channels added one after another (c = 0, 1, ..., d-1), each square and each
+// addition rounded separately (no fused multiply-add), one token per thread.
+// The squared norm orders tokens as the norm does in exact arithmetic and
+// needs no square root.  For bf16 tokens every step is exact.  A nonnegative
+// double's bit pattern orders like its value, so the key is the raw 64 bits.
+// The permutation is a stable segmented radix sort of (key, token) pairs, one
+// segment per sequence (rocPRIM's device segmented radix sort, a library
+// primitive): equal keys keep token order.
+//
+// Permutation.  Rows of any width move as 16-, 4- or 2-byte units, one unit
+// per thread: GATHER out[i] = x[perm[i]], SCATTER out[perm[i]] = x[i].
+#include <cstring>
+
+#include <rocprim/device/device_segmented_radix_sort.hpp>
+
+#include "common.h"
+
+namespace basa {
+namespace {
+
+constexpr int RANK_NT = 256;
+
+__host__ __device__ inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+template <typename T> struct Row16;  // sixteen bytes of a row as float64 values, in order
+template <> struct Row16<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const uint16_t* p, double* v) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (double)bf16_bits_to_f32(w[i] & 0xFFFFu);
+      v[2 * i + 1] = (double)bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+};
+template <> struct Row16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, double* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+template <> struct Row16<double> {
+  static constexpr int N = 2;
+  static __device__ __forceinline__ void load(const double* p, double* v) {
+    const double2 a = *reinterpret_cast<const double2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  }
+};
+
+// keys[r] = squared norm of row r (bits), vals[r] = r's position in its
+// sequence, offs[s] = s * len for s = 0 .. outer
+template <typename T>
+__global__ __launch_bounds__(RANK_NT) void norm_key_kernel(const T* x, int64_t rows, int d,
+                                                           int64_t len, int64_t outer,
+                                                           uint64_t* keys, int32_t* vals,
+                                                           int32_t* offs) {
+  const int64_t r = (int64_t)blockIdx.x * RANK_NT + threadIdx.x;
+  if (r <= outer) offs[r] = (int32_t)(r * len);
+  if (r >= rows) return;
+  const T* p = x + r * d;
+  double s = 0.0;
+  for (int c = 0; c < d; c += Row16<T>::N) {
+    double v[Row16<T>::N];
+    Row16<T>::load(p + c, v);
+#pragma unroll
+    for (int i = 0; i < Row16<T>::N; ++i) s = __dadd_rn(s, __dmul_rn(v[i], v[i]));
+  }
+  keys[r] = (uint64_t)__double_as_longlong(s);
+  vals[r] = (int32_t)(r % len);
+}
+
+template <typename U>
+__global__ __launch_bounds__(RANK_NT) void permute_kernel(const U* x, int64_t len, int64_t upr,
+                                                          int64_t units, const int32_t* perm,
+                                                          int scatter, U* out) {
+  const int64_t t = (int64_t)blockIdx.x * RANK_NT + threadIdx.x;
+  if (t >= units) return;
+  const int64_t row = t / upr, u = t - row * upr;
+  const int64_t seg0 = row - row % len;  // first row of this sequence
+  const int32_t p = perm[row];
+  const bool ok = p >= 0 && p < len;
+  if (scatter) {
+    if (ok) out[(seg0 + p) * upr + u] = x[t];
+  } else {
+    out[t] = ok ? x[(seg0 + p) * upr + u] : U{};
+  }
+}
+
+// workspace: keys in | keys out | token values | segment offsets | rocPRIM temp
+struct RankLayout {
+  int64_t keys_in, keys_out, vals, offs, temp, temp_bytes, total;
+};
+
+RankLayout rank_layout(int64_t outer, int64_t len) {
+  const int64_t n = outer * len;
+  RankLayout l;
+  l.keys_in = 0;
+  l.keys_out = align256(l.keys_in + n * 8);
+  l.vals = align256(l.keys_out + n * 8);
+  l.offs = align256(l.vals + n * 4);
+  l.temp = align256(l.offs + (outer + 1) * 4);
+  size_t tb = 0;
+  // a size query: nothing is launched and no pointer is read
+  (void)rocprim::segmented_radix_sort_pairs(nullptr, tb, (const uint64_t*)nullptr, (uint64_t*)nullptr,
+                                            (const int32_t*)nullptr, (int32_t*)nullptr,
+                                            (unsigned int)n, (unsigned int)outer,
+                                            (const int32_t*)nullptr, (const int32_t*)nullptr, 0, 64);
+  l.temp_bytes = (int64_t)tb;
+  l.total = align256(l.temp + l.temp_bytes);
+  return l;
+}
+
+}  // namespace
+
+int64_t rank_workspace_bytes(int64_t outer, int64_t len) {
+  if (outer * len == 0) return 0;
+  return rank_layout(outer, len).total;
+}
+
+hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                       int32_t* perm, void* workspace, int64_t workspace_bytes, hipStream_t s) {
+  const RankLayout l = rank_layout(outer, len);
+  if (workspace_bytes < l.total) return hipErrorInvalidValue;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint64_t* keys_in = reinterpret_cast<uint64_t*>(ws + l.keys_in);
+  uint64_t* keys_out = reinterpret_cast<uint64_t*>(ws + l.keys_out);
+  int32_t* vals = reinterpret_cast<int32_t*>(ws + l.vals);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + l.offs);
+  const int64_t rows = outer * len;
+  const int64_t threads = rows > outer + 1 ? rows : outer + 1;
+  const dim3 grid((unsigned)((threads + RANK_NT - 1) / RANK_NT));
+  const int d = (int)head_dim;
+  if (x_dtype == BASA_BF16)
+    norm_key_kernel<uint16_t><<<grid, RANK_NT, 0, s>>>(static_cast<const uint16_t*>(x), rows, d, len,
+                                                       outer, keys_in, vals, offs);
+  else if (x_dtype == BASA_F32)
+    norm_key_kernel<float><<<grid, RANK_NT, 0, s>>>(static_cast<const float*>(x), rows, d, len,
+                                                    outer, keys_in, vals, offs);
+  else
+    norm_key_kernel<double><<<grid, RANK_NT, 0, s>>>(static_cast<const double*>(x), rows, d, len,
+                                                     outer, keys_in, vals, offs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  size_t tb = (size_t)l.temp_bytes;
+  e = rocprim::segmented_radix_sort_pairs(ws + l.temp, tb, (const uint64_t*)keys_in, keys_out,
+                                          (const int32_t*)vals, perm, (unsigned int)rows,
+                                          (unsigned int)outer, (const int32_t*)offs,
+                                          (const int32_t*)(offs + 1), 0, 64, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int64_t outer, int64_t len, int64_t row_bytes,
+                          const int32_t* perm, int mode, void* out, hipStream_t s) {
+  const int scatter = mode == BASA_PERMUTE_SCATTER;
+  const int64_t rows = outer * len;
+  if (row_bytes % 16 == 0) {
+    const int64_t upr = row_bytes / 16, units = rows * upr;
+    permute_kernel<uint4><<<dim3((unsigned)((units + RANK_NT - 1) / RANK_NT)), RANK_NT, 0, s>>>(
+        static_cast<const uint4*>(x), len, upr, units, perm, scatter, static_cast<uint4*>(out));
+  } else if (row_bytes % 4 == 0) {
+    const int64_t upr = row_bytes / 4, units = rows * upr;
+    permute_kernel<uint32_t><<<dim3((unsigned)((units + RANK_NT - 1) / RANK_NT)), RANK_NT, 0, s>>>(
+        static_cast<const uint32_t*>(x), len, upr, units, perm, scatter, static_cast<uint32_t*>(out));
+  } else {
+    const int64_t upr = row_bytes / 2, units = rows * upr;
+    permute_kernel<uint16_t><<<dim3((unsigned)((units + RANK_NT - 1) / RANK_NT)), RANK_NT, 0, s>>>(
+        static_cast<const uint16_t*>(x), len, upr, units, perm, scatter, static_cast<uint16_t*>(out));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace basa

@@ -6,6 +6,9 @@ intermediate device buffers (torch) and chains the four C calls.
 * ba_forward       - BA-Att paper, section 3.1 / Algorithm 1 without sorting
                      or compensation: pool Q and K per block, score the blocks,
                      keep the top-k key blocks per query block, attend.
+* ba_forward_ranked - the same with the norm-based ranking of section 3.3
+                     (Algorithm 1 steps 1, 2 and 12): tokens reordered by l2
+                     norm before the blocks are formed, outputs mapped back.
 * llsa_forward     - log-linear sparse attention (loglinear-sparse-dit
                      README): levels of 16-token means, coarse-to-fine per-token
                      top-k, attention over fine survivors plus every coarse
@@ -20,7 +23,8 @@ import math
 
 import torch
 
-from . import (SELECT_BLOCKS, SELECT_CHANGE, basa_attn, basa_merge, basa_pool, basa_select,
+from . import (PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS, SELECT_CHANGE, basa_attn,
+               basa_merge, basa_permute, basa_pool, basa_rank, basa_rank_workspace, basa_select,
                basa_select_workspace, kv_segment)
 
 
@@ -72,6 +76,58 @@ def ba_forward(q, k, v, block: int, topk: int, scale: float | None = None):
     f = BaForward(q, k, v, block, topk, scale)
     f.run()
     return f.idx, f.o, f.lse
+
+
+class BaRankedForward:
+    """BA-Att Algorithm 1 with norm-based ranking (section 3.3) and no
+    covariance compensation (beta = 0), for fixed shapes.
+
+    rank(): perm_q orders each query head's tokens by non-decreasing l2 norm,
+    perm_k each key head's (Eq. 10, stable); Q' = Q[perm_q], K' = K[perm_k],
+    V' = V[perm_k] (steps 1 and 2).  select() and attend() run the plain
+    forward on the ranked tensors (idx indexes ranked key blocks); attend()
+    then maps O and LSE back to token order by the inverse of perm_q (step 12).
+    run() does all three and returns (o, lse).
+    """
+
+    def __init__(self, q, k, v, block: int, topk: int, scale: float | None = None,
+                 o_dtype=None):
+        b, h, length, _ = q.shape
+        hkv = k.shape[1]
+        self.q, self.k, self.v = q, k, v
+        self.perm_q = _empty(b, h, length, dtype=torch.int32, like=q)
+        self.perm_k = _empty(b, hkv, length, dtype=torch.int32, like=q)
+        need = max(basa_rank_workspace(b * h, length), basa_rank_workspace(b * hkv, length), 1)
+        self.workspace = _empty(need, dtype=torch.uint8, like=q)
+        self.qs, self.ks, self.vs = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        self.inner = BaForward(self.qs, self.ks, self.vs, block, topk, scale, o_dtype)
+        self.o = torch.empty_like(self.inner.o)
+        self.lse = torch.empty_like(self.inner.lse)
+
+    @property
+    def idx(self):
+        return self.inner.idx
+
+    def rank(self):
+        basa_rank(self.q, self.perm_q, self.workspace)
+        basa_rank(self.k, self.perm_k, self.workspace)
+        basa_permute(self.q, self.perm_q, self.qs, PERMUTE_GATHER)
+        basa_permute(self.k, self.perm_k, self.ks, PERMUTE_GATHER)
+        basa_permute(self.v, self.perm_k, self.vs, PERMUTE_GATHER)
+
+    def select(self):
+        self.inner.select()
+
+    def attend(self):
+        self.inner.attend()
+        basa_permute(self.inner.o, self.perm_q, self.o, PERMUTE_SCATTER)
+        basa_permute(self.inner.lse, self.perm_q, self.lse, PERMUTE_SCATTER)
+
+    def run(self):
+        self.rank()
+        self.select()
+        self.attend()
+        return self.o, self.lse
 
 
 # ---------------------------------------------------------------------------

@@ -10,6 +10,8 @@
  *   basa_attn    flash-style attention with an online softmax over the key
  *                blocks listed for each query tile; emits O and the LSE
  *   basa_merge   combines two partial (O, LSE) results of one row
+ *   basa_rank    orders each sequence's tokens by their l2 norm
+ *   basa_permute moves rows by such an order (gather) or back (scatter)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -243,6 +245,58 @@ int basa_attn(const basa_attn_desc* desc, const void* q, int q_dtype, void* o, i
 int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse_a,
                const void* o_b, const float* lse_b, int in_dtype, void* o, int o_dtype,
                float* lse, void* stream);
+
+/*
+ * basa_rank_workspace - bytes of device workspace basa_rank needs to rank
+ * `outer` sequences of `len` tokens (0 when outer*len == 0).
+ * Errors: BASA_E_NULLPTR for bytes == NULL; BASA_E_SHAPE as in basa_rank.
+ */
+int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes);
+
+/*
+ * basa_rank - norm-based token ranking.
+ *
+ * Follows the BA-Att paper, section 3.3 (Eq. 9 scores a token by its l2 norm,
+ * Eq. 10 orders the tokens by non-decreasing score) and Algorithm 1 steps 1
+ * and 2 (queries and keys are ranked before the blocks are formed).  Each of
+ * the `outer` sequences is ranked on its own, over all its tokens.  The key
+ * of a token is its squared norm in float64, channels added in order with
+ * every square and sum rounded separately (exact for bf16 tokens); tokens
+ * with equal keys keep their order (a stable sort).
+ *   x          device [outer][len][head_dim] of x_dtype (F32, BF16 or F64)
+ *   perm       device int32 [outer][len]: position i of sequence s holds
+ *              token perm[s][i] (an index into that sequence)
+ *   workspace  device scratch of at least basa_rank_workspace(outer, len)
+ *              bytes, caller-owned; its contents are not kept
+ * Errors: BASA_E_SHAPE for outer < 0, len < 0, outer*len above 2^31 - 1,
+ * head_dim not a multiple of 8 or above 512; BASA_E_NULLPTR for a missing
+ * pointer; BASA_E_SHAPE when workspace_bytes is too small.
+ */
+int basa_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+              int32_t* perm, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Directions of basa_permute. */
+enum {
+  BASA_PERMUTE_GATHER = 0, /* out[s][i] = x[s][perm[s][i]] (into ranked order) */
+  BASA_PERMUTE_SCATTER = 1 /* out[s][perm[s][i]] = x[s][i] (back to token order) */
+};
+
+/*
+ * basa_permute - move whole rows of each sequence by a permutation.
+ *
+ * BA-Att Algorithm 1: GATHER forms the ranked sequences Q', K', V' (steps 1
+ * and 2; V moves with K's order); SCATTER maps outputs of ranked query rows
+ * back to the original order by the inverse permutation (step 12).
+ *   x     device [outer][len][width] of dtype (F32, BF16 or F64)
+ *   perm  device int32 [outer][len], each sequence a permutation of 0..len-1
+ *         (a GATHER row whose entry is out of range is zero-filled; a
+ *         SCATTER entry out of range writes nothing)
+ *   out   device [outer][len][width] of dtype; must not overlap x
+ * Errors: BASA_E_SHAPE for negative sizes or width < 1; BASA_E_UNSUPPORTED
+ * for a mode other than the two above or overlapping x and out.
+ */
+int basa_permute(const void* x, int dtype, int64_t outer, int64_t len, int64_t width,
+                 const int32_t* perm, int mode, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -196,3 +196,50 @@ def test_binding_needs_gpu_tensors():
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         basa.basa_pool(x, 16, mean_rows=torch.zeros(1, 1, 4, 64, dtype=torch.float64))
+
+
+def rank(x=FAKE, xdt=basa.BF16, outer=2, length=256, d=128, perm=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return basa.lib.basa_rank(x, xdt, outer, length, d, perm, ws, ws_bytes, None)
+
+
+def test_rank_validation():
+    assert rank(outer=-1) == SHAPE
+    assert rank(length=-1) == SHAPE
+    assert rank(outer=1 << 16, length=1 << 16) == SHAPE  # more than 2^31 - 1 tokens
+    assert rank(d=100) == SHAPE
+    assert rank(d=4) == SHAPE
+    assert rank(d=1024) == SHAPE
+    assert rank(xdt=7) == DTYPE
+    assert rank(x=None) == NULLPTR
+    assert rank(perm=None) == NULLPTR
+    assert rank(ws=None) == NULLPTR
+    assert rank(x=MISALIGNED) == ALIGN
+    assert rank(ws=MISALIGNED) == ALIGN
+    assert rank(length=0) == OK
+    assert rank(outer=0, x=None, perm=None, ws=None) == OK
+
+
+def test_rank_workspace_validation():
+    out = ctypes.c_int64(-1)
+    assert basa.lib.basa_rank_workspace(2, 256, None) == NULLPTR
+    assert basa.lib.basa_rank_workspace(-1, 256, ctypes.byref(out)) == SHAPE
+    assert basa.lib.basa_rank_workspace(1 << 16, 1 << 16, ctypes.byref(out)) == SHAPE
+    assert basa.lib.basa_rank_workspace(0, 256, ctypes.byref(out)) == OK and out.value == 0
+
+
+def permute(x=FAKE, dt=basa.BF16, outer=2, length=256, width=128, perm=FAKE + (1 << 24), mode=0,
+            out=FAKE + (1 << 26)):
+    return basa.lib.basa_permute(x, dt, outer, length, width, perm, mode, out, None)
+
+
+def test_permute_validation():
+    assert permute(outer=-1) == SHAPE
+    assert permute(width=0) == SHAPE
+    assert permute(dt=5) == DTYPE
+    assert permute(mode=2) == UNSUPPORTED
+    assert permute(x=None) == NULLPTR
+    assert permute(perm=None) == NULLPTR
+    assert permute(out=None) == NULLPTR
+    assert permute(out=MISALIGNED + (1 << 26)) == ALIGN
+    assert permute(out=FAKE + 1024) == UNSUPPORTED  # overlaps x
+    assert permute(length=0) == OK
