@@ -120,6 +120,31 @@ def _time(torch, fn, reps=10):
     return e0.elapsed_time(e1) / reps
 
 
+def ranked_stage(torch, basa, q, k, v, w) -> dict:
+    """BA-Att with norm-based ranking (section 3.3) on the same 64K inputs:
+    ranking of Q and K (squared norms + stable segmented sort), the gathers of
+    Q, K, V into ranked order, and the whole ranked forward (rank, pool,
+    select, attend, scatter of O and LSE back to token order)."""
+    from block_sparse_attention_mean_amd.pipelines import BaRankedForward
+    f = BaRankedForward(q, k, v, w.block, w.topk, w.scale)
+    t_rank = _time(torch, lambda: (basa.basa_rank(q, f.perm_q, f.workspace),
+                                   basa.basa_rank(k, f.perm_k, f.workspace)))
+    t_gather = _time(torch, lambda: (basa.basa_permute(q, f.perm_q, f.qs),
+                                     basa.basa_permute(k, f.perm_k, f.ks),
+                                     basa.basa_permute(v, f.perm_k, f.vs)))
+    t_fwd = _time(torch, f.run, reps=5)
+    tensor = q.numel() * q.element_size()
+    flops = 4.0 * w.block ** 3 * w.heads * w.blocks * w.topk
+    out = {
+        "rank_q_k": {"ms": t_rank, "read_GB/s": 2 * tensor / (t_rank * 1e-3) / 1e9},
+        "gather_q_k_v": {"ms": t_gather, "GB/s": 6 * tensor / (t_gather * 1e-3) / 1e9,
+                         "frac_hbm": 6 * tensor / (t_gather * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "forward_ms": t_fwd, "forward_TFLOP/s": flops / (t_fwd * 1e-3) / 1e12,
+    }
+    del f
+    return out
+
+
 def llsa_and_losa_stages(torch, wl, basa) -> dict:
     """The hierarchical (log-linear) forward on the 256x256-image workload and the
     LoSA prefix step on the 64K-prefix workload."""
@@ -267,6 +292,7 @@ def main():
                            "frac_hbm": merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "max_abs_vs_one_shot": float((om.float() - o.float()).abs().max())}
         del oa, ob, la, lb, om, lm
+        stages["ranked64k"] = ranked_stage(torch, basa, q, k, v, w)
         stages.update(llsa_and_losa_stages(torch, wl, basa))
 
     result = {

@@ -7,15 +7,18 @@
 // The squared norm orders tokens as the norm does in exact arithmetic and
 // needs no square root.  For bf16 tokens every step is exact.  A nonnegative
 // double's bit pattern orders like its value, so the key is the raw 64 bits.
-// The permutation is a stable segmented radix sort of (key, token) pairs, one
-// segment per sequence (rocPRIM's device segmented radix sort, a library
-// primitive): equal keys keep token order.
+// The permutation comes from two stable device-wide radix sorts (rocPRIM, a
+// library primitive): all tokens of all sequences by key, then by sequence.
+// The second sort keeps the first one's order inside each sequence, so every
+// sequence ends up in key order with equal keys in token order.  (One
+// segmented sort would give each sequence to a single workgroup, which is
+// slow for the few long sequences of this path.)
 //
 // Permutation.  Rows of any width move as 16-, 4- or 2-byte units, one unit
 // per thread: GATHER out[i] = x[perm[i]], SCATTER out[perm[i]] = x[i].
 #include <cstring>
 
-#include <rocprim/device/device_segmented_radix_sort.hpp>
+#include <rocprim/device/device_radix_sort.hpp>
 
 #include "common.h"
 
@@ -54,15 +57,11 @@ template <> struct Row16<double> {
   }
 };
 
-// keys[r] = squared norm of row r (bits), vals[r] = r's position in its
-// sequence, offs[s] = s * len for s = 0 .. outer
+// keys[r] = squared norm of row r (bits), vals[r] = r
 template <typename T>
 __global__ __launch_bounds__(RANK_NT) void norm_key_kernel(const T* x, int64_t rows, int d,
-                                                           int64_t len, int64_t outer,
-                                                           uint64_t* keys, int32_t* vals,
-                                                           int32_t* offs) {
+                                                           uint64_t* keys, int32_t* vals) {
   const int64_t r = (int64_t)blockIdx.x * RANK_NT + threadIdx.x;
-  if (r <= outer) offs[r] = (int32_t)(r * len);
   if (r >= rows) return;
   const T* p = x + r * d;
   double s = 0.0;
@@ -73,7 +72,21 @@ __global__ __launch_bounds__(RANK_NT) void norm_key_kernel(const T* x, int64_t r
     for (int i = 0; i < Row16<T>::N; ++i) s = __dadd_rn(s, __dmul_rn(v[i], v[i]));
   }
   keys[r] = (uint64_t)__double_as_longlong(s);
-  vals[r] = (int32_t)(r % len);
+  vals[r] = (int32_t)r;
+}
+
+// seg[i] = sequence of row vals[i]
+__global__ __launch_bounds__(RANK_NT) void seq_of_kernel(const int32_t* vals, int64_t rows,
+                                                         int64_t len, uint32_t* seg) {
+  const int64_t i = (int64_t)blockIdx.x * RANK_NT + threadIdx.x;
+  if (i < rows) seg[i] = (uint32_t)(vals[i] / len);
+}
+
+// perm[i] = position of row vals[i] inside its sequence
+__global__ __launch_bounds__(RANK_NT) void local_index_kernel(const int32_t* vals, int64_t rows,
+                                                              int64_t len, int32_t* perm) {
+  const int64_t i = (int64_t)blockIdx.x * RANK_NT + threadIdx.x;
+  if (i < rows) perm[i] = (int32_t)(vals[i] % len);
 }
 
 template <typename U>
@@ -93,26 +106,38 @@ __global__ __launch_bounds__(RANK_NT) void permute_kernel(const U* x, int64_t le
   }
 }
 
-// workspace: keys in | keys out | token values | segment offsets | rocPRIM temp
+// workspace: keys in | keys out | rows | rows by key | sequences in | out |
+// rows by (sequence, key) | rocPRIM temp (the larger of the two sorts')
 struct RankLayout {
-  int64_t keys_in, keys_out, vals, offs, temp, temp_bytes, total;
+  int64_t keys_in, keys_out, vals_a, vals_b, seg_in, seg_out, vals_c, temp, temp_bytes, total;
 };
+
+int seq_bits(int64_t outer) {
+  int b = 0;
+  while (b < 31 && (int64_t(1) << b) < outer) ++b;
+  return b;
+}
 
 RankLayout rank_layout(int64_t outer, int64_t len) {
   const int64_t n = outer * len;
   RankLayout l;
   l.keys_in = 0;
   l.keys_out = align256(l.keys_in + n * 8);
-  l.vals = align256(l.keys_out + n * 8);
-  l.offs = align256(l.vals + n * 4);
-  l.temp = align256(l.offs + (outer + 1) * 4);
-  size_t tb = 0;
-  // a size query: nothing is launched and no pointer is read
-  (void)rocprim::segmented_radix_sort_pairs(nullptr, tb, (const uint64_t*)nullptr, (uint64_t*)nullptr,
-                                            (const int32_t*)nullptr, (int32_t*)nullptr,
-                                            (unsigned int)n, (unsigned int)outer,
-                                            (const int32_t*)nullptr, (const int32_t*)nullptr, 0, 64);
-  l.temp_bytes = (int64_t)tb;
+  l.vals_a = align256(l.keys_out + n * 8);
+  l.vals_b = align256(l.vals_a + n * 4);
+  l.seg_in = align256(l.vals_b + n * 4);
+  l.seg_out = align256(l.seg_in + n * 4);
+  l.vals_c = align256(l.seg_out + n * 4);
+  l.temp = align256(l.vals_c + n * 4);
+  // size queries: nothing is launched and no pointer is read
+  size_t t1 = 0, t2 = 0;
+  (void)rocprim::radix_sort_pairs(nullptr, t1, (const uint64_t*)nullptr, (uint64_t*)nullptr,
+                                  (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n, 0u,
+                                  64u);
+  (void)rocprim::radix_sort_pairs(nullptr, t2, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+                                  (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n, 0u,
+                                  (unsigned int)seq_bits(outer));
+  l.temp_bytes = (int64_t)(t1 > t2 ? t1 : t2);
   l.total = align256(l.temp + l.temp_bytes);
   return l;
 }
@@ -131,29 +156,43 @@ hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, i
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint64_t* keys_in = reinterpret_cast<uint64_t*>(ws + l.keys_in);
   uint64_t* keys_out = reinterpret_cast<uint64_t*>(ws + l.keys_out);
-  int32_t* vals = reinterpret_cast<int32_t*>(ws + l.vals);
-  int32_t* offs = reinterpret_cast<int32_t*>(ws + l.offs);
+  int32_t* vals_a = reinterpret_cast<int32_t*>(ws + l.vals_a);
+  int32_t* vals_b = reinterpret_cast<int32_t*>(ws + l.vals_b);
+  uint32_t* seg_in = reinterpret_cast<uint32_t*>(ws + l.seg_in);
+  uint32_t* seg_out = reinterpret_cast<uint32_t*>(ws + l.seg_out);
+  int32_t* vals_c = reinterpret_cast<int32_t*>(ws + l.vals_c);
   const int64_t rows = outer * len;
-  const int64_t threads = rows > outer + 1 ? rows : outer + 1;
-  const dim3 grid((unsigned)((threads + RANK_NT - 1) / RANK_NT));
+  const unsigned n = (unsigned)rows;
+  const dim3 grid((unsigned)((rows + RANK_NT - 1) / RANK_NT));
   const int d = (int)head_dim;
   if (x_dtype == BASA_BF16)
-    norm_key_kernel<uint16_t><<<grid, RANK_NT, 0, s>>>(static_cast<const uint16_t*>(x), rows, d, len,
-                                                       outer, keys_in, vals, offs);
+    norm_key_kernel<uint16_t><<<grid, RANK_NT, 0, s>>>(static_cast<const uint16_t*>(x), rows, d,
+                                                       keys_in, vals_a);
   else if (x_dtype == BASA_F32)
-    norm_key_kernel<float><<<grid, RANK_NT, 0, s>>>(static_cast<const float*>(x), rows, d, len,
-                                                    outer, keys_in, vals, offs);
+    norm_key_kernel<float><<<grid, RANK_NT, 0, s>>>(static_cast<const float*>(x), rows, d, keys_in,
+                                                    vals_a);
   else
-    norm_key_kernel<double><<<grid, RANK_NT, 0, s>>>(static_cast<const double*>(x), rows, d, len,
-                                                     outer, keys_in, vals, offs);
+    norm_key_kernel<double><<<grid, RANK_NT, 0, s>>>(static_cast<const double*>(x), rows, d,
+                                                     keys_in, vals_a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t tb = (size_t)l.temp_bytes;
-  e = rocprim::segmented_radix_sort_pairs(ws + l.temp, tb, (const uint64_t*)keys_in, keys_out,
-                                          (const int32_t*)vals, perm, (unsigned int)rows,
-                                          (unsigned int)outer, (const int32_t*)offs,
-                                          (const int32_t*)(offs + 1), 0, 64, s);
+  e = rocprim::radix_sort_pairs(ws + l.temp, tb, (const uint64_t*)keys_in, keys_out,
+                                (const int32_t*)vals_a, vals_b, n, 0u, 64u, s);
   if (e != hipSuccess) return e;
+  const int bits = seq_bits(outer);
+  const int32_t* by_seq = vals_b;
+  if (bits > 0) {
+    seq_of_kernel<<<grid, RANK_NT, 0, s>>>(vals_b, rows, len, seg_in);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tb = (size_t)l.temp_bytes;
+    e = rocprim::radix_sort_pairs(ws + l.temp, tb, (const uint32_t*)seg_in, seg_out,
+                                  (const int32_t*)vals_b, vals_c, n, 0u, (unsigned)bits, s);
+    if (e != hipSuccess) return e;
+    by_seq = vals_c;
+  }
+  local_index_kernel<<<grid, RANK_NT, 0, s>>>(by_seq, rows, len, perm);
   return hipGetLastError();
 }
 
