@@ -14,6 +14,7 @@ __all__ = [
     "sparse_attention", "dense_attention", "merge", "llsa_num_levels", "llsa_forward",
     "llsa_keys_per_query", "token_change", "active_tokens", "losa_step",
     "norm_key", "norm_rank", "gather_rows", "scatter_rows", "ba_forward_ranked",
+    "block_variance", "compensated_logits", "ba_forward_algorithm1",
 ]
 
 
@@ -265,6 +266,70 @@ def ba_forward_ranked(q, k, v, block: int, topk: int, scale: float):
     o_s, lse_s = sparse_attention(qs, ks, vs, idx, block, block, scale)
     o = scatter_rows(o_s, pq)
     lse = scatter_rows(lse_s[..., None], pq)[..., 0]
+    return pq, pk, idx, o, lse
+
+
+# ---------------------------------------------------------------------------
+# BA-Att, section 3.4 (Eq. 13-14) and Algorithm 1 steps 4, 6 and 7:
+# covariance compensation of the block logits
+# ---------------------------------------------------------------------------
+
+def block_variance(x: np.ndarray, block: int) -> np.ndarray:
+    """Population variance of every channel over each run of `block` tokens:
+    [..., L, d] -> [..., L/block, d], the mean of (x - block mean)^2.
+
+    The diagonal of the block covariance Sigma = E[dX dX^T] of BA-Att section
+    3.4 (dX the deviation from the block mean, E over the block's tokens);
+    Algorithm 1 step 4 computes it with the block means.
+    """
+    x = as_f64(x)
+    length, d = x.shape[-2], x.shape[-1]
+    xb = x.reshape(*x.shape[:-2], length // block, block, d)
+    dev = xb - xb.mean(axis=-2, keepdims=True)
+    return (dev * dev).mean(axis=-2)
+
+
+def compensated_logits(qbar, kbar, qvar, kvar, scale: float, beta: float) -> np.ndarray:
+    """BA-Att Eq. 13 with the diagonal approximation of Eq. 14, taken as printed:
+
+        l~[gq, gk] = scale * Qbar_gq . Kbar_gk + beta * Delta[gq, gk],
+        Delta = (1/d) sum_t (Var[Q_t]_gq Kbar_gk,t^2 + Var[K_t]_gk Qbar_gq,t^2
+                             + Var[Q_t]_gq Var[K_t]_gk).
+
+    qbar, qvar [B, Hq, Nq, d]; kbar, kvar [B, Hkv, Nk, d] (query head h reads
+    key head h // (Hq/Hkv)); result [B, Hq, Nq, Nk].
+    """
+    qbar, kbar, qvar, kvar = (as_f64(a) for a in (qbar, kbar, qvar, kvar))
+    group = qbar.shape[1] // kbar.shape[1]
+    if group > 1:
+        kbar = np.repeat(kbar, group, axis=1)
+        kvar = np.repeat(kvar, group, axis=1)
+    d = qbar.shape[-1]
+    t = lambda a: np.swapaxes(a, -1, -2)
+    delta = (qvar @ t(kbar * kbar) + (qbar * qbar) @ t(kvar) + qvar @ t(kvar)) / d
+    return scale * (qbar @ t(kbar)) + beta * delta
+
+
+def ba_forward_algorithm1(q, k, v, block: int, topk: int, scale: float, beta: float = 1.0,
+                          rank: bool = True):
+    """BA-Att Algorithm 1: norm ranking (steps 1-2, when rank), block means and
+    variances (step 4), compensated logits (steps 5-7), per-row top-kappa
+    (steps 8-11), block-sparse attention and the remap to token order (step
+    12).  Returns (perm_q, perm_k, idx, O, LSE); the permutations are None
+    without ranking.
+    """
+    pq = pk = None
+    qs, ks, vs = as_f64(q), as_f64(k), as_f64(v)
+    if rank:
+        pq, pk = norm_rank(q), norm_rank(k)
+        qs, ks, vs = gather_rows(qs, pq), gather_rows(ks, pk), gather_rows(vs, pk)
+    scores = compensated_logits(pool_mean(qs, block), pool_mean(ks, block),
+                                block_variance(qs, block), block_variance(ks, block), scale, beta)
+    idx = topk_ascending(scores, topk)
+    o, lse = sparse_attention(qs, ks, vs, idx, block, block, scale)
+    if rank:
+        o = scatter_rows(o, pq)
+        lse = scatter_rows(lse[..., None], pq)[..., 0]
     return pq, pk, idx, o, lse
 
 
