@@ -122,9 +122,11 @@ def _time(torch, fn, reps=10):
 
 def ranked_stage(torch, basa, q, k, v, w) -> dict:
     """BA-Att with norm-based ranking (section 3.3) on the same 64K inputs:
-    ranking of Q and K (squared norms + stable segmented sort), the gathers of
-    Q, K, V into ranked order, and the whole ranked forward (rank, pool,
-    select, attend, scatter of O and LSE back to token order)."""
+    ranking of Q and K (squared norms + stable radix sorts), the gathers of
+    Q, K, V into ranked order, the whole ranked forward (rank, pool, select,
+    attend, scatter of O and LSE back to token order), and the same with the
+    covariance compensation of section 3.4 (beta = 1): its moments + selection
+    stage and the whole Algorithm 1 forward."""
     from block_sparse_attention_mean_amd.pipelines import BaRankedForward
     f = BaRankedForward(q, k, v, w.block, w.topk, w.scale)
     t_rank = _time(torch, lambda: (basa.basa_rank(q, f.perm_q, f.workspace),
@@ -133,6 +135,12 @@ def ranked_stage(torch, basa, q, k, v, w) -> dict:
                                      basa.basa_permute(k, f.perm_k, f.ks),
                                      basa.basa_permute(v, f.perm_k, f.vs)))
     t_fwd = _time(torch, f.run, reps=5)
+    del f
+    # the whole of Algorithm 1: ranking plus covariance compensation (beta = 1)
+    g = BaRankedForward(q, k, v, w.block, w.topk, w.scale, beta=1.0)
+    g.rank()
+    t_comp_sel = _time(torch, g.select)
+    t_alg1 = _time(torch, g.run, reps=5)
     tensor = q.numel() * q.element_size()
     flops = 4.0 * w.block ** 3 * w.heads * w.blocks * w.topk
     out = {
@@ -140,8 +148,10 @@ def ranked_stage(torch, basa, q, k, v, w) -> dict:
         "gather_q_k_v": {"ms": t_gather, "GB/s": 6 * tensor / (t_gather * 1e-3) / 1e9,
                          "frac_hbm": 6 * tensor / (t_gather * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "forward_ms": t_fwd, "forward_TFLOP/s": flops / (t_fwd * 1e-3) / 1e12,
+        "compensated_pool_select_ms": t_comp_sel,
+        "algorithm1_forward_ms": t_alg1, "algorithm1_TFLOP/s": flops / (t_alg1 * 1e-3) / 1e12,
     }
-    del f
+    del g
     return out
 
 

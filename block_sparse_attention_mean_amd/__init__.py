@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_HERE, "libbasa.so")
 F32, BF16, F64 = 0, 1, 2
 SELECT_BLOCKS, SELECT_CHANGE = 0, 1
 PERMUTE_GATHER, PERMUTE_SCATTER = 0, 1
+MOMENTS_QUERY, MOMENTS_KEY = 0, 1
 
 STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE",
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
-           "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute")
+           "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments")
 
 
 class BasaError(RuntimeError):
@@ -87,6 +88,9 @@ def _load() -> ctypes.CDLL:
     lib.basa_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, i32, vp, vp]
     lib.basa_merge.restype = i32
     lib.basa_merge.argtypes = [i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp]
+    lib.basa_pool_moments.restype = i32
+    lib.basa_pool_moments.argtypes = [vp, i32, i64, i64, i64, i64, i32, ctypes.c_double,
+                                      ctypes.c_double, vp, vp]
     lib.basa_rank_workspace.restype = i32
     lib.basa_rank_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.basa_rank.restype = i32
@@ -253,6 +257,21 @@ def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b:
                                         _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
 
 
+def basa_pool_moments(x: torch.Tensor, block: int, out: torch.Tensor, role: int,
+                      scale: float = 1.0, beta: float = 1.0) -> None:
+    """Block moments of x [..., len, d] arranged for compensated scoring: QUERY
+    out [..., len/block, 3d] = [scale*mean, beta/d*var, beta/d*mean^2]; KEY out
+    [..., 3d, len/block] = [mean, mean^2+var, var] (float64)."""
+    *lead, length, d = x.shape
+    outer = 1
+    for s in lead:
+        outer *= s
+    if out.dtype != torch.float64:
+        raise TypeError("moments are float64")
+    _check("basa_pool_moments", lib.basa_pool_moments(_ptr(x), _dt(x), outer, length, d, block, role,
+                                                      float(scale), float(beta), _ptr(out), _stream()))
+
+
 def _outer_len(x: torch.Tensor, lead_dims: int) -> tuple[int, int]:
     outer = 1
     for s in x.shape[:lead_dims]:
@@ -303,4 +322,4 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
 __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
-           "PERMUTE_SCATTER"]
+           "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY"]

@@ -58,6 +58,25 @@ int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t he
   }
 }
 
+int basa_pool_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                      int64_t block, int role, double scale, double beta, double* out,
+                      void* stream) {
+  try {
+    if (outer < 0 || len < 0 || block < 1 || len % block != 0) return BASA_E_SHAPE;
+    if (head_dim < 8 || head_dim > 168 || head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (!std::isfinite(scale) || !std::isfinite(beta)) return BASA_E_SHAPE;
+    if (x_dtype != BASA_F32 && x_dtype != BASA_BF16 && x_dtype != BASA_F64) return BASA_E_DTYPE;
+    if (role != BASA_MOMENTS_QUERY && role != BASA_MOMENTS_KEY) return BASA_E_UNSUPPORTED;
+    if (outer * len == 0) return BASA_OK;
+    if (!x || !out) return BASA_E_NULLPTR;
+    if (!aligned16(x) || !aligned16(out)) return BASA_E_ALIGN;
+    return from_hip(basa::launch_moments(x, x_dtype, outer, len, head_dim, block, role, scale, beta,
+                                         out, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_select(const basa_select_desc* d, const void* q, const void* k, int dtype, int32_t* idx,
                 void* stream) {
   try {

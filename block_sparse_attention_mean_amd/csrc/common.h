@@ -97,6 +97,9 @@ hipError_t launch_attn_generic(const basa_attn_desc* d, const void* q, int q_dty
 hipError_t launch_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse_a,
                         const void* o_b, const float* lse_b, int in_dtype, void* o, int o_dtype,
                         float* lse, hipStream_t s);
+hipError_t launch_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                          int64_t block, int role, double scale, double beta, double* out,
+                          hipStream_t s);
 int64_t rank_workspace_bytes(int64_t outer, int64_t len);
 hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                        int32_t* perm, void* workspace, int64_t workspace_bytes, hipStream_t s);

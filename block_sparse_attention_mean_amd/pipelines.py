@@ -23,9 +23,9 @@ import math
 
 import torch
 
-from . import (PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS, SELECT_CHANGE, basa_attn,
-               basa_merge, basa_permute, basa_pool, basa_rank, basa_rank_workspace, basa_select,
-               basa_select_workspace, kv_segment)
+from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS,
+               SELECT_CHANGE, basa_attn, basa_merge, basa_permute, basa_pool, basa_pool_moments,
+               basa_rank, basa_rank_workspace, basa_select, basa_select_workspace, kv_segment)
 
 
 def _empty(*shape, dtype, like):
@@ -42,25 +42,37 @@ class BaForward:
     q, k, v [B, H, L, d] bf16 (or float32); block = query/key block size;
     topk = kept key blocks per query block.  run() fills self.idx (int32
     [B, H, L/block, topk], ascending), self.o and self.lse.
+
+    beta: when given, blocks are ranked by the covariance-compensated logit
+    of BA-Att Eq. 13-14 (section 3.4) with that weight: the block moments go
+    into 3d-long vectors whose dot product is the compensated logit, and the
+    same selection kernels rank them.
     """
 
     def __init__(self, q, k, v, block: int, topk: int, scale: float | None = None,
-                 o_dtype=None):
+                 o_dtype=None, beta: float | None = None):
         b, h, length, d = q.shape
         self.q, self.k, self.v = q, k, v
         self.block, self.topk = block, topk
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.beta = beta
         nb = length // block
-        self.qbar = _empty(b, h, nb, d, dtype=torch.float64, like=q)
-        self.kbt = _empty(b, k.shape[1], d, k.shape[2] // block, dtype=torch.float64, like=q)
+        width = d if beta is None else 3 * d
+        self.qbar = _empty(b, h, nb, width, dtype=torch.float64, like=q)
+        self.kbt = _empty(b, k.shape[1], width, k.shape[2] // block, dtype=torch.float64, like=q)
         self.idx = _empty(b, h, nb, topk, dtype=torch.int32, like=q)
         self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
         self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
 
     def select(self):
-        basa_pool(self.q, self.block, mean_rows=self.qbar)
-        basa_pool(self.k, self.block, mean_cols=self.kbt)
-        basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=self.scale)
+        if self.beta is None:
+            basa_pool(self.q, self.block, mean_rows=self.qbar)
+            basa_pool(self.k, self.block, mean_cols=self.kbt)
+            basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=self.scale)
+            return
+        basa_pool_moments(self.q, self.block, self.qbar, MOMENTS_QUERY, self.scale, self.beta)
+        basa_pool_moments(self.k, self.block, self.kbt, MOMENTS_KEY, 1.0, self.beta)
+        basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=1.0)
 
     def attend(self):
         basa_attn(self.q, kv_segment(self.idx, self.k, self.v), self.o, self.lse,
@@ -79,8 +91,9 @@ def ba_forward(q, k, v, block: int, topk: int, scale: float | None = None):
 
 
 class BaRankedForward:
-    """BA-Att Algorithm 1 with norm-based ranking (section 3.3) and no
-    covariance compensation (beta = 0), for fixed shapes.
+    """BA-Att Algorithm 1 with norm-based ranking (section 3.3), for fixed
+    shapes; with beta given, also the covariance compensation of section 3.4
+    (the whole of Algorithm 1), else none (beta = 0).
 
     rank(): perm_q orders each query head's tokens by non-decreasing l2 norm,
     perm_k each key head's (Eq. 10, stable); Q' = Q[perm_q], K' = K[perm_k],
@@ -91,7 +104,7 @@ class BaRankedForward:
     """
 
     def __init__(self, q, k, v, block: int, topk: int, scale: float | None = None,
-                 o_dtype=None):
+                 o_dtype=None, beta: float | None = None):
         b, h, length, _ = q.shape
         hkv = k.shape[1]
         self.q, self.k, self.v = q, k, v
@@ -100,7 +113,7 @@ class BaRankedForward:
         need = max(basa_rank_workspace(b * h, length), basa_rank_workspace(b * hkv, length), 1)
         self.workspace = _empty(need, dtype=torch.uint8, like=q)
         self.qs, self.ks, self.vs = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        self.inner = BaForward(self.qs, self.ks, self.vs, block, topk, scale, o_dtype)
+        self.inner = BaForward(self.qs, self.ks, self.vs, block, topk, scale, o_dtype, beta)
         self.o = torch.empty_like(self.inner.o)
         self.lse = torch.empty_like(self.inner.lse)
 

@@ -10,6 +10,8 @@
  *   basa_attn    flash-style attention with an online softmax over the key
  *                blocks listed for each query tile; emits O and the LSE
  *   basa_merge   combines two partial (O, LSE) results of one row
+ *   basa_pool_moments  block means and variances arranged so that the
+ *                covariance-compensated block score is one dot product
  *   basa_rank    orders each sequence's tokens by their l2 norm
  *   basa_permute moves rows by such an order (gather) or back (scatter)
  *
@@ -82,6 +84,38 @@ int basa_version(void);
 int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
               int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
               int copy_dtype, void* stream);
+
+/* Roles of basa_pool_moments. */
+enum {
+  BASA_MOMENTS_QUERY = 0, /* query blocks: rows u */
+  BASA_MOMENTS_KEY = 1    /* key blocks: transposed w */
+};
+
+/*
+ * basa_pool_moments - block statistics for covariance-compensated scores.
+ *
+ * Follows the BA-Att paper, section 3.4 (Eq. 13 adds beta * Delta to the
+ * block logit; Eq. 14 approximates Delta from per-channel block variances)
+ * and Algorithm 1 steps 4-7.  With block means Xbar and population variances
+ * Var[X] (per channel, the mean of squared deviations over the block's
+ * tokens, both in float64),
+ *   l~ = scale * Qbar.Kbar + beta * (1/d) sum_t (Var[Q_t] Kbar_t^2
+ *        + Var[K_t] Qbar_t^2 + Var[Q_t] Var[K_t])
+ * is the dot product of
+ *   u = [scale * Qbar, (beta/d) * Var[Q], (beta/d) * Qbar^2]   (QUERY role)
+ *   w = [Kbar, Kbar^2 + Var[K], Var[K]]                        (KEY role)
+ * so basa_select with head_dim 3*head_dim, scale 1 and these vectors ranks
+ * key blocks by the compensated logit.
+ *   x     device [outer][len][head_dim] of x_dtype (F32, BF16 or F64)
+ *   out   device float64: QUERY [outer][len/block][3*head_dim],
+ *         KEY [outer][3*head_dim][len/block]
+ * Errors: BASA_E_SHAPE for negative sizes, block < 1, len % block != 0,
+ * head_dim not a multiple of 8 or above 168 (3*head_dim <= 512), or a
+ * non-finite scale or beta; BASA_E_UNSUPPORTED for another role.
+ */
+int basa_pool_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                      int64_t block, int role, double scale, double beta, double* out,
+                      void* stream);
 
 /* Selection modes of basa_select. */
 enum {

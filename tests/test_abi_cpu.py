@@ -243,3 +243,23 @@ def test_permute_validation():
     assert permute(out=MISALIGNED + (1 << 26)) == ALIGN
     assert permute(out=FAKE + 1024) == UNSUPPORTED  # overlaps x
     assert permute(length=0) == OK
+
+
+def moments(x=FAKE, xdt=basa.BF16, outer=2, length=256, d=128, block=64, role=0, scale=0.1, beta=1.0,
+            out=FAKE):
+    return basa.lib.basa_pool_moments(x, xdt, outer, length, d, block, role, scale, beta, out, None)
+
+
+def test_pool_moments_validation():
+    assert moments(length=250) == SHAPE
+    assert moments(block=0) == SHAPE
+    assert moments(d=176) == SHAPE     # 3 d would exceed the selection's 512 channels
+    assert moments(d=100) == SHAPE
+    assert moments(scale=float("nan")) == SHAPE
+    assert moments(beta=float("inf")) == SHAPE
+    assert moments(xdt=9) == DTYPE
+    assert moments(role=2) == UNSUPPORTED
+    assert moments(x=None) == NULLPTR
+    assert moments(out=None) == NULLPTR
+    assert moments(out=MISALIGNED) == ALIGN
+    assert moments(outer=0, x=None, out=None) == OK

@@ -77,6 +77,34 @@ def test_ba_ranked_forward_dlm64k_full_perms_indices_sampled_tiles(pipes):
         assert max_err(lse[0, h, rows], rl) <= LSE_TOL, (h, t)
 
 
+def test_ba_algorithm1_dlm64k_full_perms_indices_sampled_tiles(pipes):
+    note("BA-Att Algorithm 1 (ranking + compensation, beta 1) dlm64k: indices full, 16 sampled tiles")
+    w = wl.WORKLOADS["dlm64k"]
+    x = wl.generate("dlm64k")
+    f = pipes.BaRankedForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.block, w.topk, beta=1.0)
+    f.run()
+    torch.cuda.synchronize()
+    pq, pk = orc.norm_rank(x["q"]), orc.norm_rank(x["k"])
+    assert np.array_equal(host(f.perm_q), pq)
+    assert np.array_equal(host(f.perm_k), pk)
+    qs = orc.gather_rows(orc.as_f64(x["q"]), pq)
+    ks = orc.gather_rows(orc.as_f64(x["k"]), pk)
+    scores = orc.compensated_logits(orc.pool_mean(qs, w.block), orc.pool_mean(ks, w.block),
+                                    orc.block_variance(qs, w.block), orc.block_variance(ks, w.block),
+                                    w.scale, 1.0)
+    ref_idx = orc.topk_ascending(scores, w.topk)
+    assert np.array_equal(host(f.idx), ref_idx)
+    vs = orc.gather_rows(x["v"], pk)
+    o, lse = host(f.o), host(f.lse)
+    g = np.random.Generator(np.random.PCG64(39))
+    for h, t in zip(g.integers(0, w.heads, 16), g.integers(0, w.blocks, 16)):
+        ranked = np.arange(t * w.block, (t + 1) * w.block)
+        ro, rl = orc.attend_rows(qs[0, h, ranked], ks[0, h], vs[0, h], ref_idx[0, h, t], w.block, w.scale)
+        rows = pq[0, h, ranked]
+        assert max_err(o[0, h, rows], ro) <= O_TOL, (h, t)
+        assert max_err(lse[0, h, rows], rl) <= LSE_TOL, (h, t)
+
+
 @pytest.mark.parametrize("n,heads,d", [(1024, 2, 64), (4096, 3, 64), (65536, 4, 64)])
 def test_llsa_forward_matches_oracle(pipes, n, heads, d):
     note(f"LLSA forward N{n} H{heads} d{d}")
