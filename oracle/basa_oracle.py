@@ -15,6 +15,7 @@ __all__ = [
     "llsa_keys_per_query", "token_change", "active_tokens", "losa_step",
     "norm_key", "norm_rank", "gather_rows", "scatter_rows", "ba_forward_ranked",
     "block_variance", "compensated_logits", "ba_forward_algorithm1",
+    "block_mass", "range_counts", "topk_in_ranges", "sparsed_pattern", "sparsed_forward",
 ]
 
 
@@ -331,6 +332,74 @@ def ba_forward_algorithm1(q, k, v, block: int, topk: int, scale: float, beta: fl
         o = scatter_rows(o, pq)
         lse = scatter_rows(lse[..., None], pq)[..., 0]
     return pq, pk, idx, o, lse
+
+
+# ---------------------------------------------------------------------------
+# Block mass of the dense attention map: BA-Att Eq. 3 (oracle block
+# distribution) and SparseD section 3.3 (average-pooled attention scores,
+# isolated top-rho% selection over prefill and generation keys, Eq. 5-6)
+# ---------------------------------------------------------------------------
+
+def block_mass(q, k, block: int, scale: float) -> np.ndarray:
+    """m^[gq, gk] = (1/|I(gq)|) sum_{i in I(gq)} sum_{j in J(gk)} A_ij, BA-Att Eq. 3,
+    with A = softmax(scale * Q K^T) the dense attention map of Eq. 1, row by
+    row over all keys.  q [B, Hq, L, d], k [B, Hkv, L, d]; result
+    [B, Hq, L/block, L/block].  SparseD's avgpool(A, block) is m^ / block.
+    """
+    q, k = as_f64(q), as_f64(k)
+    nb_, hq, length, d = q.shape
+    group = hq // k.shape[1]
+    nq, nk = length // block, k.shape[2] // block
+    out = np.empty((nb_, hq, nq, nk))
+    for b in range(nb_):
+        for h in range(hq):
+            z = scale * (q[b, h] @ k[b, h // group].T)
+            m = z.max(axis=-1, keepdims=True)
+            e = np.exp(z - m)
+            a = e / e.sum(axis=-1, keepdims=True)
+            out[b, h] = a.reshape(nq, block, nk, block).sum(axis=(1, 3)) / block
+    return out
+
+
+def range_counts(n_pre: int, n_gen: int, rho: float) -> tuple[int, int]:
+    """Blocks kept in each key range: ceil(rho * n) (at least rho of the range;
+    the pages give the fraction, not the rounding), none for an empty range."""
+    f = lambda n: 0 if n == 0 else min(n, max(1, math.ceil(rho * n - 1e-12)))
+    return f(n_pre), f(n_gen)
+
+
+def topk_in_ranges(scores, split: int, k_lo: int, k_hi: int) -> np.ndarray:
+    """Per row, the k_lo best columns of [0, split) and the k_hi best of
+    [split, n), each under (score descending, column ascending), returned
+    together in ascending column order (int32 [..., k_lo + k_hi])."""
+    scores = np.asarray(scores, dtype=np.float64)
+    lo = topk_ascending(scores[..., :split], k_lo) if k_lo else np.zeros(scores.shape[:-1] + (0,), np.int32)
+    hi = (topk_ascending(scores[..., split:], k_hi) + split) if k_hi else np.zeros(scores.shape[:-1] + (0,), np.int32)
+    return np.concatenate([lo, hi], axis=-1).astype(np.int32)
+
+
+def sparsed_pattern(q, k, block: int, scale: float, prefill: int, rho: float) -> np.ndarray:
+    """SparseD isolated selection (section 3.3, Eq. 5-6) on query/key blocks:
+    per query block, the top-rho% key blocks by average-pooled attention score
+    among the prefill keys (tokens before `prefill`) and, separately, among the
+    generation keys (the rest), united.  `prefill` must be a multiple of the
+    block (the text of Eq. 6 ends inside the generation range's bounds; they
+    are read as the complement of the prefill range)."""
+    if prefill % block:
+        raise ValueError("the prefill length must be a multiple of the block")
+    m = block_mass(q, k, block, scale)
+    split = prefill // block
+    k_lo, k_hi = range_counts(split, m.shape[-1] - split, rho)
+    return topk_in_ranges(m, split, k_lo, k_hi)
+
+
+def sparsed_forward(q, k, v, block: int, scale: float, prefill: int, rho: float):
+    """SparseD's sparse step: the pattern of sparsed_pattern (computed once from
+    a dense step and reused) applied as the block mask of Eq. 3-4.  Returns
+    (idx, O, LSE)."""
+    idx = sparsed_pattern(q, k, block, scale, prefill, rho)
+    o, lse = sparse_attention(q, k, v, idx, block, block, scale)
+    return idx, o, lse
 
 
 # ---------------------------------------------------------------------------
