@@ -155,6 +155,32 @@ def ranked_stage(torch, basa, q, k, v, w) -> dict:
     return out
 
 
+def sparsed_stage(torch, wl, basa) -> dict:
+    """SparseD (section 3.3) on the 16K DLM-shaped workload, prefill 8192,
+    rho 0.3: the dense float64 block mass of the attention map (computed once
+    per pattern), the isolated range selection, and the block-sparse attention
+    that reuses the pattern."""
+    from block_sparse_attention_mean_amd.pipelines import SparsedForward
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    w = wl.WORKLOADS["dlm16k"]
+    x = wl.generate("dlm16k")
+    f = SparsedForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.block, w.tokens // 2, 0.3, w.scale)
+    t_mass = _time(torch, lambda: basa.basa_block_mass(f.q, f.k, w.block, f.mass, f.scale), reps=2)
+    t_sel = _time(torch, lambda: basa.basa_select_ranges(f.mass, f.split, f.k_lo, f.k_hi, f.idx))
+    f.pattern()
+    t_attn = _time(torch, f.attend)
+    dense_fp64 = 2 * 2.0 * w.heads * w.tokens * w.tokens * w.head_dim  # two Q K^T passes
+    kept = f.k_lo + f.k_hi
+    out = {"block_mass_ms": t_mass, "block_mass_fp64_TFLOP/s": dense_fp64 / (t_mass * 1e-3) / 1e12,
+           "select_ranges_ms": t_sel, "kept_blocks": kept, "attn_ms": t_attn,
+           "attn_TFLOP/s": 4.0 * w.block ** 3 * w.heads * w.blocks * kept / (t_attn * 1e-3) / 1e12}
+    del f
+    return out
+
+
 def llsa_and_losa_stages(torch, wl, basa) -> dict:
     """The hierarchical (log-linear) forward on the 256x256-image workload and the
     LoSA prefix step on the 64K-prefix workload."""
@@ -303,6 +329,7 @@ def main():
                            "max_abs_vs_one_shot": float((om.float() - o.float()).abs().max())}
         del oa, ob, la, lb, om, lm
         stages["ranked64k"] = ranked_stage(torch, basa, q, k, v, w)
+        stages["sparsed16k"] = sparsed_stage(torch, wl, basa)
         stages.update(llsa_and_losa_stages(torch, wl, basa))
 
     result = {

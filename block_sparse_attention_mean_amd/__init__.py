@@ -25,7 +25,8 @@ STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
-           "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments")
+           "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
+           "basa_block_mass", "basa_select_ranges")
 
 
 class BasaError(RuntimeError):
@@ -91,6 +92,11 @@ def _load() -> ctypes.CDLL:
     lib.basa_pool_moments.restype = i32
     lib.basa_pool_moments.argtypes = [vp, i32, i64, i64, i64, i64, i32, ctypes.c_double,
                                       ctypes.c_double, vp, vp]
+    lib.basa_block_mass.restype = i32
+    lib.basa_block_mass.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                    vp, vp]
+    lib.basa_select_ranges.restype = i32
+    lib.basa_select_ranges.argtypes = [vp, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.basa_rank_workspace.restype = i32
     lib.basa_rank_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.basa_rank.restype = i32
@@ -272,6 +278,32 @@ def basa_pool_moments(x: torch.Tensor, block: int, out: torch.Tensor, role: int,
                                                       float(scale), float(beta), _ptr(out), _stream()))
 
 
+def basa_block_mass(q: torch.Tensor, k: torch.Tensor, block: int, mass: torch.Tensor,
+                    scale: float) -> None:
+    """mass [B, Hq, Lq/block, Lk/block] float64 <- the dense attention map's
+    block mass (rows sum to 1) for q [B, Hq, Lq, d], k [B, Hkv, Lk, d]."""
+    b, hq, lq, d = q.shape
+    if k.dtype != q.dtype or k.shape[0] != b or k.shape[3] != d:
+        raise TypeError("q and k must share batch, head_dim and dtype")
+    if mass.dtype != torch.float64:
+        raise TypeError("mass is float64")
+    _check("basa_block_mass", lib.basa_block_mass(_ptr(q), _ptr(k), _dt(q), b, hq, k.shape[1], lq,
+                                                  k.shape[2], d, block, float(scale), _ptr(mass),
+                                                  _stream()))
+
+
+def basa_select_ranges(scores: torch.Tensor, split: int, k_lo: int, k_hi: int,
+                       idx: torch.Tensor) -> None:
+    """idx [..., k_lo + k_hi] int32 <- per row of scores [..., n] (float64), the k_lo
+    best of columns [0, split) and the k_hi best of [split, n), ascending."""
+    if scores.dtype != torch.float64 or idx.dtype != torch.int32:
+        raise TypeError("scores are float64 and idx int32")
+    n = scores.shape[-1]
+    rows = scores.numel() // max(n, 1)
+    _check("basa_select_ranges", lib.basa_select_ranges(_ptr(scores), rows, n, split, k_lo, k_hi,
+                                                        _ptr(idx), _stream()))
+
+
 def _outer_len(x: torch.Tensor, lead_dims: int) -> tuple[int, int]:
     outer = 1
     for s in x.shape[:lead_dims]:
@@ -322,4 +354,5 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
 __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
-           "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY"]
+           "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass",
+           "basa_select_ranges"]

@@ -192,6 +192,43 @@ int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse
   }
 }
 
+int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
+                    int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim, int64_t block,
+                    double scale, double* mass, void* stream) {
+  try {
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv != 0) return BASA_E_SHAPE;
+    if (head_dim < 8 || head_dim > 128 || head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (block < 4 || block > 256 || (block & (block - 1)) != 0) return BASA_E_SHAPE;
+    if (len_q < 0 || len_k < 0 || len_q % block != 0 || len_k % block != 0) return BASA_E_SHAPE;
+    if (!(scale > 0.0) || !std::isfinite(scale)) return BASA_E_SHAPE;
+    if (dtype != BASA_F32 && dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (batch == 0 || len_q == 0 || len_k == 0) return BASA_OK;
+    if (!q || !k || !mass) return BASA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(mass)) return BASA_E_ALIGN;
+    return from_hip(basa::launch_block_mass(q, k, dtype, batch, heads_q, heads_kv, len_q, len_k,
+                                            head_dim, block, scale, mass,
+                                            static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split, int32_t k_lo,
+                       int32_t k_hi, int32_t* idx, void* stream) {
+  try {
+    if (rows < 0 || n < 1 || n > 1024 || split < 0 || split > n) return BASA_E_SHAPE;
+    if (k_lo < 0 || k_lo > split || k_hi < 0 || k_hi > n - split || k_lo + k_hi == 0)
+      return BASA_E_SHAPE;
+    if (rows == 0) return BASA_OK;
+    if (!scores || !idx) return BASA_E_NULLPTR;
+    if (!aligned16(scores) || !aligned16(idx)) return BASA_E_ALIGN;
+    return from_hip(basa::launch_select_ranges(scores, rows, n, split, k_lo, k_hi, idx,
+                                               static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes) {
   try {
     if (!bytes) return BASA_E_NULLPTR;

@@ -1,0 +1,145 @@
+// Dense block mass of the attention map (BA-Att Eq. 3, the oracle block
+// distribution; SparseD section 3.3, whose average-pooled attention scores
+// are this mass divided by the block size):
+//   m[gq][gk] = (1/block) sum_{i in gq} sum_{j in gk} A_ij,
+//   A_ij = exp(s_ij - LSE_i),  s_ij = scale * q_i . k_j,  LSE_i over all keys.
+//
+// Everything is float64: the logits (products of exact float64 widenings of
+// the bf16/float32 inputs), the row LSE and the block sums, so that a top-k
+// over the mass is decided as an exact float64 reference would decide it.
+// One workgroup per query block; each of its rows is owned by 256/block
+// consecutive threads that split every staged key chunk between them.  Pass 1
+// forms each row's LSE (online max and sum); pass 2 adds exp(s - LSE) per key
+// block, and the workgroup adds its threads' partial sums in a fixed tree.
+// This is a dense pass (the pattern it feeds is computed once and reused).
+#include "common.h"
+
+namespace basa {
+namespace {
+
+constexpr int MASS_NT = 256;
+constexpr int MASS_MAX_D = 128;
+constexpr int MASS_KC = 32;  // keys per staged chunk
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+struct MassArgs {
+  const void* q;
+  const void* k;
+  double* mass;
+  int64_t len_q, len_k;
+  int heads_q, heads_kv, d, block;
+  double scale;
+};
+
+// keys [j0, j0 + MASS_KC) of the head into LDS as float64 (rows past len_k: zero)
+template <typename T>
+__device__ __forceinline__ void stage_keys(const T* kh, int64_t len_k, int d, int64_t j0, double* kc) {
+  for (int e = threadIdx.x; e < MASS_KC * d; e += MASS_NT) {
+    const int64_t j = j0 + e / d;
+    kc[e] = j < len_k ? (double)to_f32<T>(kh[j * d + e % d]) : 0.0;
+  }
+}
+
+// channels past d hold zero in both operands' staging (q) or are never read (k)
+__device__ __forceinline__ double dot_row(const float* qr, const double* kr, int d) {
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < MASS_MAX_D; ++c)
+    if (c < d) s = __builtin_fma((double)qr[c], kr[c], s);
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(MASS_NT) void block_mass_kernel(MassArgs a) {
+  __shared__ double kc[MASS_KC * MASS_MAX_D];
+  __shared__ double red[MASS_NT];
+  const int64_t nq = a.len_q / a.block, nk = a.len_k / a.block;
+  const int64_t gq = blockIdx.x % nq;
+  const int64_t bh = blockIdx.x / nq;
+  const int h = (int)(bh % a.heads_q);
+  const int64_t b = bh / a.heads_q;
+  const int hk = h / (a.heads_q / a.heads_kv);
+  const int d = a.d;
+  const int tpr = MASS_NT / a.block;  // threads per row (block divides 256)
+  const int row = threadIdx.x / tpr, sub = threadIdx.x % tpr;
+  const T* qh = static_cast<const T*>(a.q) + ((b * a.heads_q + h) * a.len_q + gq * a.block) * d;
+  const T* kh = static_cast<const T*>(a.k) + (b * a.heads_kv + hk) * a.len_k * d;
+  float qr[MASS_MAX_D];
+#pragma unroll
+  for (int c = 0; c < MASS_MAX_D; ++c) qr[c] = c < d ? to_f32<T>(qh[(int64_t)row * d + c]) : 0.f;
+
+  // pass 1: LSE of the row over all keys (online max and sum, float64)
+  double m = -INFINITY, l = 0.0;
+  for (int64_t j0 = 0; j0 < a.len_k; j0 += MASS_KC) {
+    __syncthreads();
+    stage_keys<T>(kh, a.len_k, d, j0, kc);
+    __syncthreads();
+    for (int jj = sub; jj < MASS_KC && j0 + jj < a.len_k; jj += tpr) {
+      const double s = a.scale * dot_row(qr, kc + jj * d, d);
+      if (s > m) {
+        l = l * exp(m - s) + 1.0;
+        m = s;
+      } else {
+        l += exp(s - m);
+      }
+    }
+  }
+  // the row's tpr threads are consecutive lanes: combine their (m, l)
+  for (int off = 1; off < tpr; off <<= 1) {
+    const double mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
+    const double mn = fmax(m, mo);
+    l = (m == -INFINITY ? 0.0 : l * exp(m - mn)) + (mo == -INFINITY ? 0.0 : lo * exp(mo - mn));
+    m = mn;
+  }
+  const double lse = m + log(l);
+
+  // pass 2: per key block, the sum of exp(s - LSE) over the block's rows and keys
+  double* out = a.mass + (bh * nq + gq) * nk;
+  for (int64_t gk = 0; gk < nk; ++gk) {
+    double part = 0.0;
+    for (int64_t j0 = gk * a.block; j0 < (gk + 1) * a.block; j0 += MASS_KC) {
+      __syncthreads();
+      stage_keys<T>(kh, a.len_k, d, j0, kc);
+      __syncthreads();
+      const int64_t jend = (gk + 1) * a.block;
+      for (int jj = sub; jj < MASS_KC && j0 + jj < jend; jj += tpr)
+        part += exp(a.scale * dot_row(qr, kc + jj * d, d) - lse);
+    }
+    red[threadIdx.x] = part;
+    __syncthreads();
+    for (int w = MASS_NT / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) out[gk] = red[0] / a.block;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
+                             int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim,
+                             int64_t block, double scale, double* mass, hipStream_t s) {
+  MassArgs a;
+  a.q = q;
+  a.k = k;
+  a.mass = mass;
+  a.len_q = len_q;
+  a.len_k = len_k;
+  a.heads_q = (int)heads_q;
+  a.heads_kv = (int)heads_kv;
+  a.d = (int)head_dim;
+  a.block = (int)block;
+  a.scale = scale;
+  const dim3 grid((unsigned)(batch * heads_q * (len_q / block)));
+  if (dtype == BASA_BF16)
+    block_mass_kernel<uint16_t><<<grid, MASS_NT, 0, s>>>(a);
+  else
+    block_mass_kernel<float><<<grid, MASS_NT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace basa

@@ -450,6 +450,54 @@ __global__ __launch_bounds__(256) void select_split_kernel(SelArgs a, int64_t gr
 }
 
 // ---------------------------------------------------------------------------
+// Top-k in two column ranges of given float64 scores (SparseD section 3.3,
+// Eq. 5-6: the prefill keys [0, split) and the generation keys [split, n)
+// are selected separately, k_lo and k_hi of them).  One wave per row, the
+// same wave top-k as above, once per range; the kept columns of both ranges
+// are written together in ascending order.
+// ---------------------------------------------------------------------------
+template <int KPL>
+__global__ __launch_bounds__(256) void select_ranges_kernel(const double* scores, int64_t rows, int n,
+                                                            int split, int k_lo, int k_hi,
+                                                            int32_t* idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const double* s = scores + row * n;
+  uint64_t key[KPL];
+  bool lo[KPL], hi[KPL], sel_lo[KPL], sel_hi[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int c = lane + 64 * j;
+    key[j] = c < n ? ordered_key(s[c]) : 0ull;
+    lo[j] = c < split;
+    hi[j] = c >= split && c < n;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (k_lo > 0) {
+    wave_topk<KPL>(key, lo, k_lo, below, sel_lo);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sel_lo[j] = false;
+  }
+  if (k_hi > 0) {
+    wave_topk<KPL>(key, hi, k_hi, below, sel_hi);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sel_hi[j] = false;
+  }
+  int32_t* out = idx + row * (k_lo + k_hi);
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool keep = sel_lo[j] || sel_hi[j];
+    const uint64_t m = __ballot(keep);
+    if (keep) out[base + popc64(m & below)] = lane + 64 * j;
+    base += popc64(m);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-staged rows (exactly 64*KPL keys, no parent list): a workgroup per 16
 // rows of one head, four per wave, four workgroups per CU.  The key means are
 // read once per workgroup: chunks of 4 channels x all keys go from global
@@ -923,6 +971,23 @@ hipError_t launch_select_change(const basa_select_desc* d, const void* q, const 
     select_change_kernel<double><<<grid, 256, 0, s>>>(static_cast<const double*>(q),
                                                       static_cast<const double*>(k), H, T, D,
                                                       d->topk, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split,
+                                int k_lo, int k_hi, int32_t* idx, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const int nn = (int)n, sp = (int)split;
+  if (n <= 64)
+    select_ranges_kernel<1><<<grid, 256, 0, s>>>(scores, rows, nn, sp, k_lo, k_hi, idx);
+  else if (n <= 128)
+    select_ranges_kernel<2><<<grid, 256, 0, s>>>(scores, rows, nn, sp, k_lo, k_hi, idx);
+  else if (n <= 256)
+    select_ranges_kernel<4><<<grid, 256, 0, s>>>(scores, rows, nn, sp, k_lo, k_hi, idx);
+  else if (n <= 512)
+    select_ranges_kernel<8><<<grid, 256, 0, s>>>(scores, rows, nn, sp, k_lo, k_hi, idx);
+  else
+    select_ranges_kernel<16><<<grid, 256, 0, s>>>(scores, rows, nn, sp, k_lo, k_hi, idx);
   return hipGetLastError();
 }
 

@@ -9,6 +9,9 @@ intermediate device buffers (torch) and chains the four C calls.
 * ba_forward_ranked - the same with the norm-based ranking of section 3.3
                      (Algorithm 1 steps 1, 2 and 12): tokens reordered by l2
                      norm before the blocks are formed, outputs mapped back.
+* SparsedForward   - SparseD section 3.3: block pattern from the dense
+                     attention map's block mass, top-rho% of prefill and of
+                     generation key blocks per query block, reused.
 * llsa_forward     - log-linear sparse attention (loglinear-sparse-dit
                      README): levels of 16-token means, coarse-to-fine per-token
                      top-k, attention over fine survivors plus every coarse
@@ -24,8 +27,9 @@ import math
 import torch
 
 from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS,
-               SELECT_CHANGE, basa_attn, basa_merge, basa_permute, basa_pool, basa_pool_moments,
-               basa_rank, basa_rank_workspace, basa_select, basa_select_workspace, kv_segment)
+               SELECT_CHANGE, basa_attn, basa_block_mass, basa_merge, basa_permute, basa_pool,
+               basa_pool_moments, basa_rank, basa_rank_workspace, basa_select, basa_select_ranges,
+               basa_select_workspace, kv_segment)
 
 
 def _empty(*shape, dtype, like):
@@ -139,6 +143,60 @@ class BaRankedForward:
     def run(self):
         self.rank()
         self.select()
+        self.attend()
+        return self.o, self.lse
+
+
+# ---------------------------------------------------------------------------
+# SparseD isolated selection and pattern reuse
+# ---------------------------------------------------------------------------
+
+def range_counts(n_pre: int, n_gen: int, rho: float) -> tuple[int, int]:
+    """Blocks kept per key range: ceil(rho * n), at least one of a non-empty range."""
+    f = lambda n: 0 if n == 0 else min(n, max(1, math.ceil(rho * n - 1e-12)))
+    return f(n_pre), f(n_gen)
+
+
+class SparsedForward:
+    """SparseD (section 3.3) for fixed shapes.
+
+    pattern(): the dense attention map's block mass (BA-Att Eq. 3; SparseD's
+    avgpool(A, block) ranks the same way), then per query block the top
+    rho of the prefill key blocks (tokens before `prefill`) and, separately,
+    of the generation key blocks, united (Eq. 5-6).  attend(q, k, v): block-
+    sparse attention under that pattern; later denoising steps reuse it by
+    calling attend with their own q, k, v.
+    """
+
+    def __init__(self, q, k, v, block: int, prefill: int, rho: float, scale: float | None = None,
+                 o_dtype=None):
+        b, h, length, d = q.shape
+        if prefill % block:
+            raise ValueError("the prefill length must be a multiple of the block")
+        self.q, self.k, self.v = q, k, v
+        self.block = block
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        nq, nk = length // block, k.shape[2] // block
+        self.split = prefill // block
+        self.k_lo, self.k_hi = range_counts(self.split, nk - self.split, rho)
+        self.mass = _empty(b, h, nq, nk, dtype=torch.float64, like=q)
+        self.idx = _empty(b, h, nq, self.k_lo + self.k_hi, dtype=torch.int32, like=q)
+        self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
+        self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
+
+    def pattern(self):
+        basa_block_mass(self.q, self.k, self.block, self.mass, self.scale)
+        basa_select_ranges(self.mass, self.split, self.k_lo, self.k_hi, self.idx)
+
+    def attend(self, q=None, k=None, v=None):
+        q = self.q if q is None else q
+        k = self.k if k is None else k
+        v = self.v if v is None else v
+        basa_attn(q, kv_segment(self.idx, k, v), self.o, self.lse, tile_q=self.block,
+                  block_k=self.block, scale=self.scale)
+
+    def run(self):
+        self.pattern()
         self.attend()
         return self.o, self.lse
 

@@ -12,6 +12,8 @@
  *   basa_merge   combines two partial (O, LSE) results of one row
  *   basa_pool_moments  block means and variances arranged so that the
  *                covariance-compensated block score is one dot product
+ *   basa_block_mass    block mass of the dense attention map
+ *   basa_select_ranges top-k of given scores in two column ranges
  *   basa_rank    orders each sequence's tokens by their l2 norm
  *   basa_permute moves rows by such an order (gather) or back (scatter)
  *
@@ -279,6 +281,46 @@ int basa_attn(const basa_attn_desc* desc, const void* q, int q_dtype, void* o, i
 int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse_a,
                const void* o_b, const float* lse_b, int in_dtype, void* o, int o_dtype,
                float* lse, void* stream);
+
+/*
+ * basa_block_mass - how much attention each query block puts on each key
+ * block, from the dense attention map.
+ *
+ * Follows the BA-Att paper, section 3.1, Eq. 3 (the oracle block
+ * distribution): m[gq][gk] = (1/block) sum over the block's query rows i and
+ * key columns j of A_ij, with A = softmax(scale * Q K^T) row by row over all
+ * keys (Eq. 1).  SparseD section 3.3 ranks blocks by the average-pooled
+ * attention scores, which are m / block.  Logits, row LSE and sums are float64
+ * (exact widenings of the inputs); each row of m sums to 1.
+ *   q     device [batch][heads_q][len_q][head_dim] of dtype (BF16 or F32)
+ *   k     device [batch][heads_kv][len_k][head_dim] of dtype; query head h
+ *         reads key head h / (heads_q / heads_kv)
+ *   mass  device float64 [batch][heads_q][len_q/block][len_k/block]
+ * A dense pass: it costs two scale*Q*K^T products in float64.
+ * Errors: BASA_E_SHAPE for non-positive heads, heads_q not a multiple of
+ * heads_kv, head_dim not a multiple of 8 or above 128, block not a power of
+ * two in [4, 256], lengths not multiples of block, or a scale that is not
+ * finite and positive.
+ */
+int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
+                    int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim, int64_t block,
+                    double scale, double* mass, void* stream);
+
+/*
+ * basa_select_ranges - per row, the best columns of two column ranges.
+ *
+ * Follows SparseD section 3.3 (Eq. 5-6, isolated selection): the top
+ * entries among the prefill keys and among the generation keys are taken
+ * separately and united.  For each row r of scores [rows][n] (float64): the
+ * k_lo best columns of [0, split) and the k_hi best of [split, n), each under
+ * (score descending, column ascending), written together in ascending column
+ * order to idx [rows][k_lo + k_hi] (int32).
+ * Errors: BASA_E_SHAPE for rows < 0, n outside [1, 1024], split outside
+ * [0, n], k_lo outside [0, split], k_hi outside [0, n - split] or
+ * k_lo + k_hi == 0.
+ */
+int basa_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split, int32_t k_lo,
+                       int32_t k_hi, int32_t* idx, void* stream);
 
 /*
  * basa_rank_workspace - bytes of device workspace basa_rank needs to rank

@@ -263,3 +263,37 @@ def test_pool_moments_validation():
     assert moments(out=None) == NULLPTR
     assert moments(out=MISALIGNED) == ALIGN
     assert moments(outer=0, x=None, out=None) == OK
+
+
+def mass(q=FAKE, k=FAKE, dt=basa.BF16, b=1, hq=4, hkv=2, lq=256, lk=256, d=64, block=32, scale=0.1,
+         out=FAKE):
+    return basa.lib.basa_block_mass(q, k, dt, b, hq, hkv, lq, lk, d, block, scale, out, None)
+
+
+def test_block_mass_validation():
+    assert mass(hq=3) == SHAPE
+    assert mass(d=136) == SHAPE
+    assert mass(block=2) == SHAPE
+    assert mass(block=48) == SHAPE
+    assert mass(lq=250) == SHAPE
+    assert mass(scale=0.0) == SHAPE
+    assert mass(dt=basa.F64) == DTYPE
+    assert mass(k=None) == NULLPTR
+    assert mass(out=MISALIGNED) == ALIGN
+    assert mass(b=0, q=None, k=None, out=None) == OK
+
+
+def ranges(s=FAKE, rows=4, n=128, split=64, lo=20, hi=20, idx=FAKE):
+    return basa.lib.basa_select_ranges(s, rows, n, split, lo, hi, idx, None)
+
+
+def test_select_ranges_validation():
+    assert ranges(n=0) == SHAPE
+    assert ranges(n=2000) == SHAPE
+    assert ranges(split=129) == SHAPE
+    assert ranges(lo=65) == SHAPE
+    assert ranges(hi=65) == SHAPE
+    assert ranges(lo=0, hi=0) == SHAPE
+    assert ranges(s=None) == NULLPTR
+    assert ranges(idx=MISALIGNED) == ALIGN
+    assert ranges(rows=0, s=None, idx=None) == OK
