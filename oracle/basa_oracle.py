@@ -16,6 +16,7 @@ __all__ = [
     "norm_key", "norm_rank", "gather_rows", "scatter_rows", "ba_forward_ranked",
     "block_variance", "compensated_logits", "ba_forward_algorithm1",
     "block_mass", "range_counts", "topk_in_ranges", "sparsed_pattern", "sparsed_forward",
+    "block_radius_maxnorm", "deviation_bound", "selection_recall",
 ]
 
 
@@ -400,6 +401,46 @@ def sparsed_forward(q, k, v, block: int, scale: float, prefill: int, rho: float)
     idx = sparsed_pattern(q, k, block, scale, prefill, rho)
     o, lse = sparse_attention(q, k, v, idx, block, block, scale)
     return idx, o, lse
+
+
+# ---------------------------------------------------------------------------
+# Fidelity diagnostics: BA-Att Eq. 7-8 (block radii, max norms and the bound
+# on the token/block logit deviation) and recall against the oracle block
+# distribution of Eq. 3
+# ---------------------------------------------------------------------------
+
+def block_radius_maxnorm(x, block: int):
+    """BA-Att Eq. 7: per block, R = max_i ||x_i - xbar||_2 (radius around the
+    block mean) and M = max_i ||x_i||_2 (largest token norm).  [..., L, d] ->
+    two [..., L/block] arrays."""
+    x = as_f64(x)
+    length, d = x.shape[-2], x.shape[-1]
+    xb = x.reshape(*x.shape[:-2], length // block, block, d)
+    dev = xb - xb.mean(axis=-2, keepdims=True)
+    r = np.sqrt((dev * dev).sum(axis=-1)).max(axis=-1)
+    m = np.sqrt((xb * xb).sum(axis=-1)).max(axis=-1)
+    return r, m
+
+
+def deviation_bound(rq, mq, rk, mk, d: int) -> np.ndarray:
+    """BA-Att Eq. 8: U[gq, gk] = (R^Q M^K + M^Q R^K + R^Q R^K) / sqrt(d), the
+    bound on |token logit - block logit| inside block pair (gq, gk) (scale
+    1/sqrt(d)).  rq, mq [..., Nq]; rk, mk [..., Nk] (same leading shape)."""
+    rq, mq, rk, mk = (np.asarray(a, dtype=np.float64)[..., :, None] if i < 2 else
+                      np.asarray(a, dtype=np.float64)[..., None, :] for i, a in enumerate((rq, mq, rk, mk)))
+    return (rq * mk + mq * rk + rq * rk) / math.sqrt(d)
+
+
+def selection_recall(idx, mass) -> float:
+    """Mean over rows of |S ∩ S*| / k: S the selected blocks idx [..., k], S*
+    the k blocks of largest oracle block mass (BA-Att Eq. 3) in the same row
+    (ties to the lower index)."""
+    idx = np.asarray(idx)
+    k = idx.shape[-1]
+    best = topk_ascending(mass, k)
+    hits = [len(set(a.tolist()) & set(b.tolist())) for a, b in
+            zip(idx.reshape(-1, k), best.reshape(-1, k))]
+    return float(np.mean(hits)) / k
 
 
 # ---------------------------------------------------------------------------
