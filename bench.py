@@ -181,6 +181,53 @@ def sparsed_stage(torch, wl, basa) -> dict:
     return out
 
 
+def fidelity_stage(torch, wl, basa) -> dict:
+    """Fidelity diagnostics on the 16K DLM-shaped workload (BA-Att Eq. 3 and
+    Eq. 7-8): for the plain, norm-ranked and Algorithm 1 (ranked and
+    compensated, beta 1) selections, the recall of each query block's kept
+    set against the top-k of the dense block mass of its own block partition,
+    and the mean over block pairs of the logit-deviation bound U of Eq. 8.
+    Kernels compute the selections, masses, top-k and block radii; the host
+    only counts set overlaps and averages."""
+    import math
+    import block_sparse_attention_mean_amd.pipelines as pl
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    w = wl.WORKLOADS["dlm16k"]
+    x = wl.generate("dlm16k")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    nb, kk = w.blocks, w.topk
+    mass = torch.empty(1, w.heads, nb, nb, dtype=torch.float64, device="cuda")
+    best = torch.empty(1, w.heads, nb, kk, dtype=torch.int32, device="cuda")
+    rad_q = torch.empty(1, w.heads, nb, 2, dtype=torch.float64, device="cuda")
+    rad_k = torch.empty_like(rad_q)
+    out = {}
+    for name, beta, ranked in (("plain", None, False), ("ranked", None, True), ("algorithm1", 1.0, True)):
+        if ranked:
+            f = pl.BaRankedForward(q, k, v, w.block, kk, w.scale, beta=beta)
+            f.rank()
+            qp, kp = f.qs, f.ks
+        else:
+            f = pl.BaForward(q, k, v, w.block, kk, w.scale)
+            qp, kp = q, k
+        f.select()
+        basa.basa_block_mass(qp, kp, w.block, mass, w.scale)
+        basa.basa_select_ranges(mass, nb, kk, 0, best)
+        basa.basa_block_radius(qp, w.block, rad_q)
+        basa.basa_block_radius(kp, w.block, rad_k)
+        torch.cuda.synchronize()
+        idx, top = f.idx.cpu().numpy(), best.cpu().numpy()
+        hits = (idx[..., :, None] == top[..., None, :]).any(-1).sum(-1)
+        rq, mq = rad_q[..., 0].mean(-1).cpu().numpy(), rad_q[..., 1].mean(-1).cpu().numpy()
+        rk, mk = rad_k[..., 0].mean(-1).cpu().numpy(), rad_k[..., 1].mean(-1).cpu().numpy()
+        u = (rq * mk + mq * rk + rq * rk) / math.sqrt(w.head_dim)  # mean over pairs, per head
+        out[name] = {"recall_vs_block_mass_topk": float(hits.mean()) / kk, "mean_U": float(u.mean())}
+        del f
+    return out
+
+
 def llsa_and_losa_stages(torch, wl, basa) -> dict:
     """The hierarchical (log-linear) forward on the 256x256-image workload and the
     LoSA prefix step on the 64K-prefix workload."""
@@ -330,6 +377,7 @@ def main():
         del oa, ob, la, lb, om, lm
         stages["ranked64k"] = ranked_stage(torch, basa, q, k, v, w)
         stages["sparsed16k"] = sparsed_stage(torch, wl, basa)
+        stages["fidelity16k"] = fidelity_stage(torch, wl, basa)
         stages.update(llsa_and_losa_stages(torch, wl, basa))
 
     result = {

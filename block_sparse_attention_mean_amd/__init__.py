@@ -26,7 +26,7 @@ STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
-           "basa_block_mass", "basa_select_ranges")
+           "basa_block_mass", "basa_select_ranges", "basa_block_radius")
 
 
 class BasaError(RuntimeError):
@@ -97,6 +97,8 @@ def _load() -> ctypes.CDLL:
                                     vp, vp]
     lib.basa_select_ranges.restype = i32
     lib.basa_select_ranges.argtypes = [vp, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.basa_block_radius.restype = i32
+    lib.basa_block_radius.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp]
     lib.basa_rank_workspace.restype = i32
     lib.basa_rank_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.basa_rank.restype = i32
@@ -304,6 +306,19 @@ def basa_select_ranges(scores: torch.Tensor, split: int, k_lo: int, k_hi: int,
                                                         _ptr(idx), _stream()))
 
 
+def basa_block_radius(x: torch.Tensor, block: int, out: torch.Tensor) -> None:
+    """out [..., len/block, 2] float64 <- per block of x [..., len, d]: (max distance of a
+    token from the block mean, max token norm)."""
+    *lead, length, d = x.shape
+    outer = 1
+    for s in lead:
+        outer *= s
+    if out.dtype != torch.float64:
+        raise TypeError("out is float64")
+    _check("basa_block_radius", lib.basa_block_radius(_ptr(x), _dt(x), outer, length, d, block,
+                                                      _ptr(out), _stream()))
+
+
 def _outer_len(x: torch.Tensor, lead_dims: int) -> tuple[int, int]:
     outer = 1
     for s in x.shape[:lead_dims]:
@@ -355,4 +370,4 @@ __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "ba
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
            "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass",
-           "basa_select_ranges"]
+           "basa_select_ranges", "basa_block_radius"]

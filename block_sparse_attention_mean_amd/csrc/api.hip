@@ -229,6 +229,22 @@ int basa_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t sp
   }
 }
 
+int basa_block_radius(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                      int64_t block, double* out, void* stream) {
+  try {
+    if (outer < 0 || len < 0 || block < 1 || block > 256 || len % block != 0) return BASA_E_SHAPE;
+    if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (x_dtype != BASA_F32 && x_dtype != BASA_BF16 && x_dtype != BASA_F64) return BASA_E_DTYPE;
+    if (outer * len == 0) return BASA_OK;
+    if (!x || !out) return BASA_E_NULLPTR;
+    if (!aligned16(x) || !aligned16(out)) return BASA_E_ALIGN;
+    return from_hip(basa::launch_radius(x, x_dtype, outer, len, head_dim, block, out,
+                                        static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes) {
   try {
     if (!bytes) return BASA_E_NULLPTR;

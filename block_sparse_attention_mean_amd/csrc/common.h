@@ -105,6 +105,8 @@ hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t ba
                              int64_t block, double scale, double* mass, hipStream_t s);
 hipError_t launch_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split,
                                 int k_lo, int k_hi, int32_t* idx, hipStream_t s);
+hipError_t launch_radius(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                         int64_t block, double* out, hipStream_t s);
 int64_t rank_workspace_bytes(int64_t outer, int64_t len);
 hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                        int32_t* perm, void* workspace, int64_t workspace_bytes, hipStream_t s);

@@ -22,6 +22,7 @@ namespace {
 
 constexpr int MOM_NT = 256;
 constexpr int MOM_MAX_D = 168;  // 3 d <= 512, the selection's largest head_dim
+constexpr int MOM_MAX_D_R = 256;  // block radii: one thread per channel for the mean
 
 template <typename T> struct Chunk8;
 template <> struct Chunk8<uint16_t> {
@@ -113,7 +114,67 @@ __global__ __launch_bounds__(MOM_NT) void moments_kernel(const T* x, int64_t len
   }
 }
 
+// BA-Att Eq. 7 per block: R = max_i ||x_i - xbar|| and M = max_i ||x_i||.
+// The mean as in moments_kernel; then one thread per token forms its two
+// squared norms (channels in order) and the workgroup takes their maxima.
+template <typename T>
+__global__ __launch_bounds__(MOM_NT) void radius_kernel(const T* x, int64_t len, int d, int block,
+                                                        double* out) {
+  __shared__ double part[MOM_NT * 8];
+  __shared__ double mean[MOM_MAX_D_R];
+  __shared__ double r2[MOM_NT], n2[MOM_NT];
+  const int64_t nb = len / block;
+  const int64_t o = blockIdx.x / nb, g = blockIdx.x % nb;
+  const int n_cg = d / 8, n_rg = MOM_NT / n_cg;
+  const int cg = threadIdx.x % n_cg, rg = threadIdx.x / n_cg;
+  const T* xb = x + (o * len + g * block) * d;
+  block_sum<T>(xb, d, block, cg, rg, n_cg, n_rg, rg < n_rg, [](double v, int) { return v; }, part, mean);
+  if ((int)threadIdx.x < d) mean[threadIdx.x] = mean[threadIdx.x] / block;
+  __syncthreads();
+  double a = 0.0, b = 0.0;
+  if ((int)threadIdx.x < block) {
+    const T* xr = xb + (int64_t)threadIdx.x * d;
+    for (int c = 0; c < d; c += 8) {
+      double v[8];
+      Chunk8<T>::load(xr + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double e = v[i] - mean[c + i];
+        a += e * e;
+        b += v[i] * v[i];
+      }
+    }
+  }
+  r2[threadIdx.x] = a;
+  n2[threadIdx.x] = b;
+  __syncthreads();
+  for (int w = MOM_NT / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      r2[threadIdx.x] = fmax(r2[threadIdx.x], r2[threadIdx.x + w]);
+      n2[threadIdx.x] = fmax(n2[threadIdx.x], n2[threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[(o * nb + g) * 2] = sqrt(r2[0]);
+    out[(o * nb + g) * 2 + 1] = sqrt(n2[0]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_radius(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                         int64_t block, double* out, hipStream_t s) {
+  const dim3 grid((unsigned)(outer * (len / block)));
+  const int d = (int)head_dim, b = (int)block;
+  if (x_dtype == BASA_BF16)
+    radius_kernel<uint16_t><<<grid, MOM_NT, 0, s>>>(static_cast<const uint16_t*>(x), len, d, b, out);
+  else if (x_dtype == BASA_F32)
+    radius_kernel<float><<<grid, MOM_NT, 0, s>>>(static_cast<const float*>(x), len, d, b, out);
+  else
+    radius_kernel<double><<<grid, MOM_NT, 0, s>>>(static_cast<const double*>(x), len, d, b, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                           int64_t block, int role, double scale, double beta, double* out,

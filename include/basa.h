@@ -14,6 +14,7 @@
  *                covariance-compensated block score is one dot product
  *   basa_block_mass    block mass of the dense attention map
  *   basa_select_ranges top-k of given scores in two column ranges
+ *   basa_block_radius  per-block radius and largest token norm
  *   basa_rank    orders each sequence's tokens by their l2 norm
  *   basa_permute moves rows by such an order (gather) or back (scatter)
  *
@@ -321,6 +322,22 @@ int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int6
  */
 int basa_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split, int32_t k_lo,
                        int32_t k_hi, int32_t* idx, void* stream);
+
+/*
+ * basa_block_radius - block geometry of the deviation bound.
+ *
+ * Follows the BA-Att paper, section 3.2, Eq. 7: for each block of `block`
+ * consecutive tokens, R = max_i ||x_i - xbar||_2 (the radius around the block
+ * mean) and M = max_i ||x_i||_2 (the largest token norm), in float64.  Eq. 8
+ * bounds the gap between a token logit and its block logit by
+ * (R^Q M^K + M^Q R^K + R^Q R^K) / sqrt(d).
+ *   x    device [outer][len][head_dim] of x_dtype (F32, BF16 or F64)
+ *   out  device float64 [outer][len/block][2] = (R, M)
+ * Errors: BASA_E_SHAPE for negative sizes, block outside [1, 256], len not a
+ * multiple of block, head_dim not a multiple of 8 or above 256.
+ */
+int basa_block_radius(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
+                      int64_t block, double* out, void* stream);
 
 /*
  * basa_rank_workspace - bytes of device workspace basa_rank needs to rank

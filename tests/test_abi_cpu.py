@@ -297,3 +297,19 @@ def test_select_ranges_validation():
     assert ranges(s=None) == NULLPTR
     assert ranges(idx=MISALIGNED) == ALIGN
     assert ranges(rows=0, s=None, idx=None) == OK
+
+
+def radius(x=FAKE, xdt=basa.BF16, outer=2, length=256, d=128, block=64, out=FAKE):
+    return basa.lib.basa_block_radius(x, xdt, outer, length, d, block, out, None)
+
+
+def test_block_radius_validation():
+    assert radius(block=0) == SHAPE
+    assert radius(block=512, length=512) == SHAPE
+    assert radius(length=250) == SHAPE
+    assert radius(d=264) == SHAPE
+    assert radius(d=12) == SHAPE
+    assert radius(xdt=4) == DTYPE
+    assert radius(out=None) == NULLPTR
+    assert radius(x=MISALIGNED) == ALIGN
+    assert radius(outer=0, x=None, out=None) == OK
