@@ -12,6 +12,8 @@
 // forms each row's LSE (online max and sum); pass 2 adds exp(s - LSE) per key
 // block, and the workgroup adds its threads' partial sums in a fixed tree.
 // This is a dense pass (the pattern it feeds is computed once and reused).
+// Blocks of 16..128 rows (multiples of 16) take the float64 MFMA kernel
+// below; other blocks take this one-thread-per-row kernel.
 #include "common.h"
 
 namespace basa {
@@ -118,6 +120,143 @@ __global__ __launch_bounds__(MASS_NT) void block_mass_kernel(MassArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same mass on the float64 matrix core (v_mfma_f64_16x16x4f64), for
+// blocks of 16..128 rows that are multiples of 16 and head_dim <= 128.  Each
+// wave owns 16-row query tiles (tile w, w+4, ...); for channel step s the
+// A operand of lane l is Q[row0 + l%16][4s + l/16] (kept in registers), the
+// B operand K[j0 + l%16][4s + l/16] (from LDS), and lane l receives the
+// logits of rows row0 + l/16 + 4r (r = 0..3) at key j0 + l%16.  Keys are
+// staged in LDS as float64 with a row stride of head_dim + 2 doubles, which
+// spreads the 16 keys x 2 channel groups a half-wave reads over all banks.
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int MM_TILES = 2;              // 16-row tiles per wave (blocks up to 128 rows)
+constexpr int MM_STEPS = MASS_MAX_D / 4;  // channel steps of 4
+
+template <typename T, int KC>
+__device__ __forceinline__ void stage_keys_padded(const T* kh, int64_t len_k, int d, int64_t j0,
+                                                  double* kc) {
+  const int str = d + 2;
+  for (int e = threadIdx.x; e < KC * d; e += MASS_NT) {
+    const int jj = e / d, c = e % d;
+    const int64_t j = j0 + jj;
+    kc[jj * str + c] = j < len_k ? (double)to_f32<T>(kh[j * d + c]) : 0.0;
+  }
+}
+
+// the 16x16 logits of tile t against the 16 keys of sub-tile u of the staged chunk
+__device__ __forceinline__ f64x4 tile_logits(const double (*aq)[MM_STEPS], int t, const double* kc,
+                                             int u, int d, int lane) {
+  const int str = d + 2;
+  const double* kb = kc + (u * 16 + (lane & 15)) * str + (lane >> 4);
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < MM_STEPS; ++s)
+    if (4 * s < d) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aq[t][s], kb[4 * s], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename T, int KC>
+__global__ __launch_bounds__(MASS_NT) void block_mass_mfma_kernel(MassArgs a) {
+  __shared__ double kc[KC * (MASS_MAX_D + 2)];
+  __shared__ double red[MASS_NT / 64];
+  const int64_t nq = a.len_q / a.block, nk = a.len_k / a.block;
+  const int64_t gq = blockIdx.x % nq;
+  const int64_t bh = blockIdx.x / nq;
+  const int h = (int)(bh % a.heads_q);
+  const int64_t b = bh / a.heads_q;
+  const int hk = h / (a.heads_q / a.heads_kv);
+  const int d = a.d, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = a.block / 16;
+  const T* qh = static_cast<const T*>(a.q) + ((b * a.heads_q + h) * a.len_q + gq * a.block) * d;
+  const T* kh = static_cast<const T*>(a.k) + (b * a.heads_kv + hk) * a.len_k * d;
+  double aq[MM_TILES][MM_STEPS];
+#pragma unroll
+  for (int t = 0; t < MM_TILES; ++t) {
+    const int tile = wave + 4 * t;
+#pragma unroll
+    for (int s = 0; s < MM_STEPS; ++s)
+      aq[t][s] = (tile < n_tiles && 4 * s < d)
+                     ? (double)to_f32<T>(qh[(int64_t)(tile * 16 + (lane & 15)) * d + 4 * s + (lane >> 4)])
+                     : 0.0;
+  }
+
+  // pass 1: per row, online max and sum of exp over all keys (lane: rows lane/16 + 4r)
+  double m[MM_TILES][4], l[MM_TILES][4];
+#pragma unroll
+  for (int t = 0; t < MM_TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[t][r] = -INFINITY;
+      l[t][r] = 0.0;
+    }
+  for (int64_t j0 = 0; j0 < a.len_k; j0 += KC) {
+    __syncthreads();
+    stage_keys_padded<T, KC>(kh, a.len_k, d, j0, kc);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MM_TILES; ++t) {
+      if (wave + 4 * t >= n_tiles) continue;  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < KC / 16; ++u) {
+        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double v = a.scale * sv[r];
+          if (v > m[t][r]) {
+            l[t][r] = l[t][r] * exp(m[t][r] - v) + 1.0;
+            m[t][r] = v;
+          } else {
+            l[t][r] += exp(v - m[t][r]);
+          }
+        }
+      }
+    }
+  }
+  // the 16 lanes of a group hold one row's keys: combine their (m, l)
+  double lse[MM_TILES][4];
+#pragma unroll
+  for (int t = 0; t < MM_TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double mm = m[t][r], ll = l[t][r];
+      for (int off = 1; off < 16; off <<= 1) {
+        const double mo = __shfl_xor(mm, off), lo = __shfl_xor(ll, off);
+        const double mn = fmax(mm, mo);
+        ll = (mm == -INFINITY ? 0.0 : ll * exp(mm - mn)) + (mo == -INFINITY ? 0.0 : lo * exp(mo - mn));
+        mm = mn;
+      }
+      lse[t][r] = mm + log(ll);
+    }
+
+  // pass 2: per key block, the sum of exp(s - LSE) over the query block
+  double* out = a.mass + (bh * nq + gq) * nk;
+  for (int64_t gk = 0; gk < nk; ++gk) {
+    double part = 0.0;
+    for (int64_t j0 = gk * a.block; j0 < (gk + 1) * a.block; j0 += KC) {
+      __syncthreads();
+      stage_keys_padded<T, KC>(kh, a.len_k, d, j0, kc);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < MM_TILES; ++t) {
+        if (wave + 4 * t >= n_tiles) continue;
+#pragma unroll
+        for (int u = 0; u < KC / 16; ++u) {
+          const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part += exp(a.scale * sv[r] - lse[t][r]);
+        }
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) out[gk] = (red[0] + red[1] + red[2] + red[3]) / a.block;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
@@ -135,10 +274,22 @@ hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t ba
   a.block = (int)block;
   a.scale = scale;
   const dim3 grid((unsigned)(batch * heads_q * (len_q / block)));
-  if (dtype == BASA_BF16)
+  const bool mfma = block % 16 == 0 && block <= 16 * 4 * MM_TILES && head_dim % 4 == 0;
+  if (mfma && block % 32 == 0) {
+    if (dtype == BASA_BF16)
+      block_mass_mfma_kernel<uint16_t, 32><<<grid, MASS_NT, 0, s>>>(a);
+    else
+      block_mass_mfma_kernel<float, 32><<<grid, MASS_NT, 0, s>>>(a);
+  } else if (mfma) {
+    if (dtype == BASA_BF16)
+      block_mass_mfma_kernel<uint16_t, 16><<<grid, MASS_NT, 0, s>>>(a);
+    else
+      block_mass_mfma_kernel<float, 16><<<grid, MASS_NT, 0, s>>>(a);
+  } else if (dtype == BASA_BF16) {
     block_mass_kernel<uint16_t><<<grid, MASS_NT, 0, s>>>(a);
-  else
+  } else {
     block_mass_kernel<float><<<grid, MASS_NT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
