@@ -3,7 +3,8 @@
 //
 // Ranking.  Every token gets a sort key: its squared l2 norm in float64, the
 // channels added one after another (c = 0, 1, ..., d-1), each square and each
-// addition rounded separately (no fused multiply-add), one token per thread.
+// addition rounded separately (no fused multiply-add), one token per thread
+// (rows of up to 512 bytes are first copied to LDS with coalesced loads).
 // The squared norm orders tokens as the norm does in exact arithmetic and
 // needs no square root.  For bf16 tokens every step is exact.  A nonnegative
 // double's bit pattern orders like its value, so the key is the raw 64 bits.
@@ -71,6 +72,37 @@ __global__ __launch_bounds__(RANK_NT) void norm_key_kernel(const T* x, int64_t r
 #pragma unroll
     for (int i = 0; i < Row16<T>::N; ++i) s = __dadd_rn(s, __dmul_rn(v[i], v[i]));
   }
+  keys[r] = (uint64_t)__double_as_longlong(s);
+  vals[r] = (int32_t)r;
+}
+
+// The same keys with coalesced reads: a workgroup copies 64 whole rows (at
+// most 512 bytes each) into LDS with consecutive 16-byte loads, then one
+// thread per row adds its squares from LDS in the same channel order.
+constexpr int NK_ROWS = 64;
+constexpr int NK_MAX_ROW = 512;  // bytes
+
+template <typename T>
+__global__ __launch_bounds__(RANK_NT) void norm_key_staged_kernel(const T* x, int64_t rows, int d,
+                                                                  uint64_t* keys, int32_t* vals) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[NK_ROWS * (NK_MAX_ROW + 16)];
+  const int row_bytes = d * (int)sizeof(T), stride = row_bytes + 16, upr = row_bytes / 16;
+  const int64_t r0 = (int64_t)blockIdx.x * NK_ROWS;
+  const int n_rows = rows - r0 < NK_ROWS ? (int)(rows - r0) : NK_ROWS;
+  const uint4* src = reinterpret_cast<const uint4*>(x + r0 * d);
+  for (int u = threadIdx.x; u < n_rows * upr; u += RANK_NT)
+    *reinterpret_cast<uint4*>(tile + (u / upr) * stride + (u % upr) * 16) = src[u];
+  __syncthreads();
+  if ((int)threadIdx.x >= n_rows) return;
+  const T* p = reinterpret_cast<const T*>(tile + threadIdx.x * stride);
+  double s = 0.0;
+  for (int c = 0; c < d; c += Row16<T>::N) {
+    double v[Row16<T>::N];
+    Row16<T>::load(p + c, v);
+#pragma unroll
+    for (int i = 0; i < Row16<T>::N; ++i) s = __dadd_rn(s, __dmul_rn(v[i], v[i]));
+  }
+  const int64_t r = r0 + threadIdx.x;
   keys[r] = (uint64_t)__double_as_longlong(s);
   vals[r] = (int32_t)r;
 }
@@ -165,15 +197,28 @@ hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, i
   const unsigned n = (unsigned)rows;
   const dim3 grid((unsigned)((rows + RANK_NT - 1) / RANK_NT));
   const int d = (int)head_dim;
-  if (x_dtype == BASA_BF16)
+  const int esize = x_dtype == BASA_BF16 ? 2 : (x_dtype == BASA_F32 ? 4 : 8);
+  if (d * esize <= NK_MAX_ROW) {
+    const dim3 sgrid((unsigned)((rows + NK_ROWS - 1) / NK_ROWS));
+    if (x_dtype == BASA_BF16)
+      norm_key_staged_kernel<uint16_t><<<sgrid, RANK_NT, 0, s>>>(static_cast<const uint16_t*>(x), rows,
+                                                                 d, keys_in, vals_a);
+    else if (x_dtype == BASA_F32)
+      norm_key_staged_kernel<float><<<sgrid, RANK_NT, 0, s>>>(static_cast<const float*>(x), rows, d,
+                                                              keys_in, vals_a);
+    else
+      norm_key_staged_kernel<double><<<sgrid, RANK_NT, 0, s>>>(static_cast<const double*>(x), rows, d,
+                                                               keys_in, vals_a);
+  } else if (x_dtype == BASA_BF16) {
     norm_key_kernel<uint16_t><<<grid, RANK_NT, 0, s>>>(static_cast<const uint16_t*>(x), rows, d,
                                                        keys_in, vals_a);
-  else if (x_dtype == BASA_F32)
+  } else if (x_dtype == BASA_F32) {
     norm_key_kernel<float><<<grid, RANK_NT, 0, s>>>(static_cast<const float*>(x), rows, d, keys_in,
                                                     vals_a);
-  else
+  } else {
     norm_key_kernel<double><<<grid, RANK_NT, 0, s>>>(static_cast<const double*>(x), rows, d,
                                                      keys_in, vals_a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t tb = (size_t)l.temp_bytes;

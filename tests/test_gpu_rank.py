@@ -155,3 +155,14 @@ def test_ranked_forward_dlm16k_full_indices_sampled_tiles(basa):
         rows = pq[0, h, ranked]  # where those ranked rows live in token order
         assert max_err(o[0, h, rows], ro) <= O_TOL, (h, t)
         assert max_err(lse[0, h, rows], rl) <= LSE_TOL, (h, t)
+
+
+@pytest.mark.parametrize("kind,shape", [("bf16", (1, 2, 300, 512)), ("f64", (2, 1, 257, 128)),
+                                        ("bf16", (1, 1, 130, 256))])
+def test_rank_wide_rows_match_oracle(basa, kind, shape):
+    # rows above 512 bytes take the one-thread-per-row kernel; 512 exactly is staged
+    note(f"rank wide rows {kind} {shape}")
+    g = np.random.Generator(np.random.PCG64(shape[-1] + shape[-2]))
+    raw = g.standard_normal(shape) * g.uniform(0.1, 3.0, shape[:-1] + (1,))
+    x = wl.f32_to_bf16(raw.astype(np.float32)) if kind == "bf16" else raw
+    assert np.array_equal(gpu_rank(basa, x), orc.norm_rank(x))
