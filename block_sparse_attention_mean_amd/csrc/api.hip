@@ -249,7 +249,9 @@ int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes) {
   try {
     if (!bytes) return BASA_E_NULLPTR;
     if (outer < 0 || len < 0 || (len > 0 && outer > INT32_MAX / len)) return BASA_E_SHAPE;
-    *bytes = basa::rank_workspace_bytes(outer, len);
+    const int64_t need = basa::rank_workspace_bytes(outer, len);
+    if (need < 0) return BASA_E_LAUNCH;  // the sort library could not size its storage
+    *bytes = need;
     return BASA_OK;
   } catch (...) {
     return BASA_E_LAUNCH;
@@ -265,7 +267,9 @@ int basa_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t he
     if (outer * len == 0) return BASA_OK;
     if (!x || !perm || !workspace) return BASA_E_NULLPTR;
     if (!aligned16(x) || !aligned16(perm) || !aligned16(workspace)) return BASA_E_ALIGN;
-    if (workspace_bytes < basa::rank_workspace_bytes(outer, len)) return BASA_E_SHAPE;
+    const int64_t need = basa::rank_workspace_bytes(outer, len);
+    if (need < 0) return BASA_E_LAUNCH;
+    if (workspace_bytes < need) return BASA_E_SHAPE;
     return from_hip(basa::launch_rank(x, x_dtype, outer, len, head_dim, perm, workspace,
                                       workspace_bytes, static_cast<hipStream_t>(stream)));
   } catch (...) {

@@ -142,6 +142,7 @@ __global__ __launch_bounds__(RANK_NT) void permute_kernel(const U* x, int64_t le
 // rows by (sequence, key) | rocPRIM temp (the larger of the two sorts')
 struct RankLayout {
   int64_t keys_in, keys_out, vals_a, vals_b, seg_in, seg_out, vals_c, temp, temp_bytes, total;
+  hipError_t status;  // of rocPRIM's size queries
 };
 
 int seq_bits(int64_t outer) {
@@ -163,12 +164,13 @@ RankLayout rank_layout(int64_t outer, int64_t len) {
   l.temp = align256(l.vals_c + n * 4);
   // size queries: nothing is launched and no pointer is read
   size_t t1 = 0, t2 = 0;
-  (void)rocprim::radix_sort_pairs(nullptr, t1, (const uint64_t*)nullptr, (uint64_t*)nullptr,
-                                  (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n, 0u,
-                                  64u);
-  (void)rocprim::radix_sort_pairs(nullptr, t2, (const uint32_t*)nullptr, (uint32_t*)nullptr,
-                                  (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n, 0u,
-                                  (unsigned int)seq_bits(outer));
+  l.status = rocprim::radix_sort_pairs(nullptr, t1, (const uint64_t*)nullptr, (uint64_t*)nullptr,
+                                       (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n,
+                                       0u, 64u);
+  if (l.status == hipSuccess && seq_bits(outer) > 0)
+    l.status = rocprim::radix_sort_pairs(nullptr, t2, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+                                         (const int32_t*)nullptr, (int32_t*)nullptr, (unsigned int)n,
+                                         0u, (unsigned int)seq_bits(outer));
   l.temp_bytes = (int64_t)(t1 > t2 ? t1 : t2);
   l.total = align256(l.temp + l.temp_bytes);
   return l;
@@ -178,12 +180,14 @@ RankLayout rank_layout(int64_t outer, int64_t len) {
 
 int64_t rank_workspace_bytes(int64_t outer, int64_t len) {
   if (outer * len == 0) return 0;
-  return rank_layout(outer, len).total;
+  const RankLayout l = rank_layout(outer, len);
+  return l.status == hipSuccess ? l.total : -1;
 }
 
 hipError_t launch_rank(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                        int32_t* perm, void* workspace, int64_t workspace_bytes, hipStream_t s) {
   const RankLayout l = rank_layout(outer, len);
+  if (l.status != hipSuccess) return l.status;
   if (workspace_bytes < l.total) return hipErrorInvalidValue;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint64_t* keys_in = reinterpret_cast<uint64_t*>(ws + l.keys_in);

@@ -342,7 +342,8 @@ int basa_block_radius(const void* x, int x_dtype, int64_t outer, int64_t len, in
 /*
  * basa_rank_workspace - bytes of device workspace basa_rank needs to rank
  * `outer` sequences of `len` tokens (0 when outer*len == 0).
- * Errors: BASA_E_NULLPTR for bytes == NULL; BASA_E_SHAPE as in basa_rank.
+ * Errors: BASA_E_NULLPTR for bytes == NULL; BASA_E_SHAPE as in basa_rank;
+ * BASA_E_LAUNCH if the HIP runtime cannot size the sort's storage.
  */
 int basa_rank_workspace(int64_t outer, int64_t len, int64_t* bytes);
 
