@@ -570,3 +570,22 @@ def test_ba_path_matches_cpp_reference(basa):
     rmo, rml = cref.merge(oa, la, ob, lb)
     assert max_err(host(om), rmo) <= O_TOL and max_err(host(lm), rml) <= 1e-5
     assert max_err(host(om), ro) <= O_TOL and max_err(host(lm), rl) <= LSE_TOL
+
+
+def test_attn_mfma_longest_list(basa):
+    """The largest list the MFMA path takes: 1023 of 1024 key blocks (131072
+    keys), every stage's block index read from the LDS copy of the list; one
+    head, sampled tiles against the oracle."""
+    note("attn mfma: kept 1023 of 1024 blocks, 1 head, L 131072")
+    x = wl.make_dlm(45, heads=1, tokens=131072, head_dim=128)
+    nb, kept, scale = 1024, 1023, 1 / math.sqrt(128)
+    g = np.random.Generator(np.random.PCG64(46))
+    idx = np.stack([np.sort(g.permutation(nb)[:kept]) for _ in range(nb)]).astype(np.int32)[None, None]
+    o, lse = run_attn(basa, x["q"], [(idx, x["k"], x["v"], {})], 128, 128, scale, torch.bfloat16)
+    tiles = [0, 511, 1023]
+    ro, rl = orc.sparse_attention(x["q"], x["k"], x["v"], idx, 128, 128, scale,
+                                  lists=[(0, 0, t) for t in tiles])
+    sel = ~np.isnan(rl)
+    assert sel.sum() == 3 * 128
+    assert max_err(o[sel], ro[sel]) <= O_TOL
+    assert max_err(lse[sel], rl[sel]) <= LSE_TOL
