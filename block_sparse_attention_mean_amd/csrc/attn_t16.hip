@@ -319,7 +319,7 @@ __device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Se
 // F32: some segment has a float32 table (without it the float32 path, and its
 // registers, are not compiled in)
 template <bool O_BF16, int D, bool F32>
-__global__ __launch_bounds__(NW * 64) void attn_t16_kernel(T16Args a) {
+__global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 3) void attn_t16_kernel(T16Args a) {
   constexpr int CPL = D / 4;
   // per-wave areas; with float32 segments also the shared area, which they alias
   // (the shared segments are done, behind a barrier, before any per-wave area is used)
