@@ -142,10 +142,62 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int6
   }
 }
 
+// Short blocks (up to 32 rows): one thread per (block, 8-channel group) adds
+// the block's rows itself, so a workgroup covers 256 / (head_dim/8) blocks
+// and no partial sums go through LDS.  Consecutive threads read consecutive
+// 16-byte pieces of the same row.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_short_kernel(const T* __restrict__ x, int64_t len, int d,
+                                                         int block, int64_t nb, int64_t n_items,
+                                                         double* __restrict__ mean_rows,
+                                                         double* __restrict__ mean_cols,
+                                                         void* __restrict__ mean_copy,
+                                                         int copy_dtype) {
+  const int64_t item = ((int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x) * 256 + threadIdx.x;
+  if (item >= n_items) return;
+  const int cols8 = d >> 3;
+  const int c8 = (int)(item % cols8);
+  const int64_t gb = item / cols8;  // block over all sequences
+  const int64_t o = gb / nb, g = gb - o * nb;
+  const T* src = x + (o * len + g * (int64_t)block) * d + c8 * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int r = 0;
+  for (; r + 8 <= block; r += 8) {  // eight row loads in flight, then their adds in row order
+    typename Load8<T>::Raw raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = Load8<T>::load(src + (int64_t)(r + u) * d);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Load8<T>::add(raw[u], acc);
+  }
+  for (; r < block; ++r) Load8<T>::add(Load8<T>::load(src + (int64_t)r * d), acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c8 * 8 + i;
+    const double mean = acc[i] / (double)block;
+    if (mean_rows) mean_rows[(o * nb + g) * d + c] = mean;
+    if (mean_cols) mean_cols[(o * d + c) * nb + g] = mean;
+    if (mean_copy) {
+      if (copy_dtype == BASA_F32)
+        reinterpret_cast<float*>(mean_copy)[(o * nb + g) * d + c] = (float)mean;
+      else
+        reinterpret_cast<uint16_t*>(mean_copy)[(o * nb + g) * d + c] = f64_to_bf16_bits(mean);
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const T* x, int64_t outer, int64_t len, int d, int block, double* mean_rows,
                         double* mean_cols, void* mean_copy, int copy_dtype, hipStream_t s) {
   const int64_t nb = len / block;
+  if (block <= 32) {
+    const int64_t n_items = outer * nb * (d / 8);
+    const int64_t n_wg = (n_items + 255) / 256;
+    const int64_t gx = n_wg < 65536 ? n_wg : 65536;
+    dim3 grid((unsigned)gx, (unsigned)((n_wg + gx - 1) / gx));
+    pool_short_kernel<T><<<grid, 256, 0, s>>>(x, len, d, block, nb, n_items, mean_rows, mean_cols,
+                                              mean_copy, copy_dtype);
+    return hipGetLastError();
+  }
   // two consecutive blocks per workgroup when the count allows (bf16 and
   // float32 inputs): twice the loads in flight per thread (the 64K pooling:
   // 194 -> 178 us); four blocks need 64 KB of LDS per workgroup and measured
