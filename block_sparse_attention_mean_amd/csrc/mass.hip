@@ -128,22 +128,65 @@ __global__ __launch_bounds__(MASS_NT) void block_mass_kernel(MassArgs a) {
 // B operand K[j0 + l%16][4s + l/16] (from LDS), and lane l receives the
 // logits of rows row0 + l/16 + 4r (r = 0..3) at key j0 + l%16.  Keys are
 // staged in LDS as float64 with a row stride of head_dim + 2 doubles, which
-// spreads the 16 keys x 2 channel groups a half-wave reads over all banks.
+// spreads the 16 keys x 2 channel groups a half-wave reads over all banks,
+// in two buffers: the loads of chunk c + 1 are in flight while chunk c is
+// multiplied, and one barrier per chunk separates them.
 // ---------------------------------------------------------------------------
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int MM_TILES = 2;              // 16-row tiles per wave (blocks up to 128 rows)
 constexpr int MM_STEPS = MASS_MAX_D / 4;  // channel steps of 4
 
+// One chunk of KC keys in flight: thread t holds the 8-channel groups t,
+// t + 256, ... of the chunk (16-byte loads of bf16, 32 of float32), issued a
+// chunk ahead and written to LDS as float64 (row stride head_dim + 2) once the
+// current chunk is done, so the matrix core does not wait on the loads.
 template <typename T, int KC>
-__device__ __forceinline__ void stage_keys_padded(const T* kh, int64_t len_k, int d, int64_t j0,
-                                                  double* kc) {
-  const int str = d + 2;
-  for (int e = threadIdx.x; e < KC * d; e += MASS_NT) {
-    const int jj = e / d, c = e % d;
-    const int64_t j = j0 + jj;
-    kc[jj * str + c] = j < len_k ? (double)to_f32<T>(kh[j * d + c]) : 0.0;
+struct KeyStage {
+  static constexpr int NG = KC / 16;            // groups per thread (head_dim <= 128)
+  static constexpr int W = sizeof(T) / 2;       // 16-byte words per group of 8 values
+  uint4 raw[NG][W];
+  __device__ __forceinline__ void load(const T* kh, int d, int64_t j0) {
+    const int gpr = d >> 3;  // groups per key
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int g = threadIdx.x + i * MASS_NT;
+      if (g < KC * gpr) {
+        const uint4* src = reinterpret_cast<const uint4*>(kh + (j0 + g / gpr) * d + (g % gpr) * 8);
+#pragma unroll
+        for (int w = 0; w < W; ++w) raw[i][w] = src[w];
+      }
+    }
   }
-}
+  __device__ __forceinline__ void store(double* kc, int d) const {
+    const int gpr = d >> 3, str = d + 2;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int g = threadIdx.x + i * MASS_NT;
+      if (g < KC * gpr) {
+        double v[8];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t wd[4] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = (double)bf16_bits_to_f32(wd[e] & 0xFFFFu);
+            v[2 * e + 1] = (double)bf16_bits_to_f32(wd[e] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            v[4 * w] = (double)__uint_as_float(raw[i][w].x);
+            v[4 * w + 1] = (double)__uint_as_float(raw[i][w].y);
+            v[4 * w + 2] = (double)__uint_as_float(raw[i][w].z);
+            v[4 * w + 3] = (double)__uint_as_float(raw[i][w].w);
+          }
+        }
+        double2* dst = reinterpret_cast<double2*>(kc + (g / gpr) * str + (g % gpr) * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = double2{v[2 * e], v[2 * e + 1]};
+      }
+    }
+  }
+};
 
 // the 16x16 logits of tile t against the 16 keys of sub-tile u of the staged chunk
 __device__ __forceinline__ f64x4 tile_logits(const double (*aq)[MM_STEPS], int t, const double* kc,
@@ -158,9 +201,10 @@ __device__ __forceinline__ f64x4 tile_logits(const double (*aq)[MM_STEPS], int t
 }
 
 template <typename T, int KC>
-__global__ __launch_bounds__(MASS_NT) void block_mass_mfma_kernel(MassArgs a) {
-  __shared__ double kc[KC * (MASS_MAX_D + 2)];
-  __shared__ double red[MASS_NT / 64];
+__global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a) {
+  __shared__ double kc0[KC * (MASS_MAX_D + 2)];
+  __shared__ double kc1[KC * (MASS_MAX_D + 2)];
+  __shared__ double red[2][MASS_NT / 64];
   const int64_t nq = a.len_q / a.block, nk = a.len_k / a.block;
   const int64_t gq = blockIdx.x % nq;
   const int64_t bh = blockIdx.x / nq;
@@ -192,10 +236,14 @@ __global__ __launch_bounds__(MASS_NT) void block_mass_mfma_kernel(MassArgs a) {
       m[t][r] = -INFINITY;
       l[t][r] = 0.0;
     }
-  for (int64_t j0 = 0; j0 < a.len_k; j0 += KC) {
-    __syncthreads();
-    stage_keys_padded<T, KC>(kh, a.len_k, d, j0, kc);
-    __syncthreads();
+  const int64_t n_chunks = a.len_k / KC;  // len_k is a multiple of block, block of KC
+  KeyStage<T, KC> st;
+  st.load(kh, d, 0);
+  st.store(kc0, d);
+  __syncthreads();
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const double* kc = (c & 1) ? kc1 : kc0;
+    if (c + 1 < n_chunks) st.load(kh, d, (c + 1) * KC);
 #pragma unroll
     for (int t = 0; t < MM_TILES; ++t) {
       if (wave + 4 * t >= n_tiles) continue;  // wave-uniform
@@ -214,6 +262,8 @@ __global__ __launch_bounds__(MASS_NT) void block_mass_mfma_kernel(MassArgs a) {
         }
       }
     }
+    if (c + 1 < n_chunks) st.store((c & 1) ? kc0 : kc1, d);
+    __syncthreads();
   }
   // the 16 lanes of a group hold one row's keys: combine their (m, l)
   double lse[MM_TILES][4];
@@ -231,29 +281,39 @@ __global__ __launch_bounds__(MASS_NT) void block_mass_mfma_kernel(MassArgs a) {
       lse[t][r] = mm + log(ll);
     }
 
-  // pass 2: per key block, the sum of exp(s - LSE) over the query block
+  // pass 2: per key block, the sum of exp(s - LSE) over the query block; the
+  // chunks run in key order and each key block's sum is closed after its last
   double* out = a.mass + (bh * nq + gq) * nk;
-  for (int64_t gk = 0; gk < nk; ++gk) {
-    double part = 0.0;
-    for (int64_t j0 = gk * a.block; j0 < (gk + 1) * a.block; j0 += KC) {
-      __syncthreads();
-      stage_keys_padded<T, KC>(kh, a.len_k, d, j0, kc);
-      __syncthreads();
+  const int64_t cpb = a.block / KC;  // chunks per key block
+  st.load(kh, d, 0);
+  st.store(kc0, d);
+  __syncthreads();
+  double part = 0.0;
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const double* kc = (c & 1) ? kc1 : kc0;
+    if (c + 1 < n_chunks) st.load(kh, d, (c + 1) * KC);
 #pragma unroll
-      for (int t = 0; t < MM_TILES; ++t) {
-        if (wave + 4 * t >= n_tiles) continue;
+    for (int t = 0; t < MM_TILES; ++t) {
+      if (wave + 4 * t >= n_tiles) continue;
 #pragma unroll
-        for (int u = 0; u < KC / 16; ++u) {
-          const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
+      for (int u = 0; u < KC / 16; ++u) {
+        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) part += exp(a.scale * sv[r] - lse[t][r]);
-        }
+        for (int r = 0; r < 4; ++r) part += exp(a.scale * sv[r] - lse[t][r]);
       }
     }
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-    if (lane == 0) red[wave] = part;
+    const bool closes = (c + 1) % cpb == 0;
+    const int64_t gk = c / cpb;
+    if (closes) {
+      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+      if (lane == 0) red[gk & 1][wave] = part;
+      part = 0.0;
+    }
+    if (c + 1 < n_chunks) st.store((c & 1) ? kc0 : kc1, d);
     __syncthreads();
-    if (threadIdx.x == 0) out[gk] = (red[0] + red[1] + red[2] + red[3]) / a.block;
+    // red[gk & 1] is written again two key blocks later, after another barrier
+    if (closes && threadIdx.x == 0)
+      out[gk] = (red[gk & 1][0] + red[gk & 1][1] + red[gk & 1][2] + red[gk & 1][3]) / a.block;
   }
 }
 
