@@ -80,6 +80,46 @@ __device__ __forceinline__ void block_sum(const T* xb, int d, int block, int cg,
   __syncthreads();
 }
 
+// bf16 blocks whose rows fit MOM_ROWS per thread: the rows are read once into
+// registers (16 bytes per row and thread) and both sums run over them, in the
+// same order as block_sum, so the moments equal the two-read form bit for bit.
+constexpr int MOM_ROWS = 8;
+
+__device__ __forceinline__ void bf16x8_to_f64(uint4 a, double* v) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = (double)bf16_bits_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = (double)bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <typename F>
+__device__ __forceinline__ void cached_sum(const uint4* raw, int n_rows, int d, int cg, int rg,
+                                           int n_rg, bool active, F f, double* part, double* tot) {
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < MOM_ROWS; ++i) {
+      if (i < n_rows) {
+        double v[8];
+        bf16x8_to_f64(raw[i], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += f(v[e], 8 * cg + e);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg * d + 8 * cg + e] = acc[e];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < d) {
+    double s = 0.0;
+    for (int g = 0; g < n_rg; ++g) s += part[g * d + threadIdx.x];
+    tot[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
 template <typename T>
 __global__ __launch_bounds__(MOM_NT) void moments_kernel(const T* x, int64_t len, int d, int block,
                                                          int key_role, double scale, double beta,
@@ -93,11 +133,28 @@ __global__ __launch_bounds__(MOM_NT) void moments_kernel(const T* x, int64_t len
   const int cg = threadIdx.x % n_cg, rg = threadIdx.x / n_cg;
   const bool active = rg < n_rg;
   const T* xb = x + (o * len + g * block) * d;
-  block_sum<T>(xb, d, block, cg, rg, n_cg, n_rg, active, [](double v, int) { return v; }, part, mean);
-  if ((int)threadIdx.x < d) mean[threadIdx.x] = mean[threadIdx.x] / block;
-  __syncthreads();
-  block_sum<T>(xb, d, block, cg, rg, n_cg, n_rg, active,
-               [&](double v, int c) { const double e = v - mean[c]; return e * e; }, part, var);
+  const int my_rows = active && rg < block ? (block - rg + n_rg - 1) / n_rg : 0;
+  const int rows_max = (block + n_rg - 1) / n_rg;  // the same for every thread
+  if constexpr (sizeof(T) == 2) {
+    if (rows_max <= MOM_ROWS) {
+      uint4 raw[MOM_ROWS];
+#pragma unroll
+      for (int i = 0; i < MOM_ROWS; ++i)
+        if (i < my_rows) raw[i] = *reinterpret_cast<const uint4*>(xb + (int64_t)(rg + i * n_rg) * d + 8 * cg);
+      cached_sum(raw, my_rows, d, cg, rg, n_rg, active, [](double v, int) { return v; }, part, mean);
+      if ((int)threadIdx.x < d) mean[threadIdx.x] = mean[threadIdx.x] / block;
+      __syncthreads();
+      cached_sum(raw, my_rows, d, cg, rg, n_rg, active,
+                 [&](double v, int c) { const double e = v - mean[c]; return e * e; }, part, var);
+    }
+  }
+  if (sizeof(T) != 2 || rows_max > MOM_ROWS) {
+    block_sum<T>(xb, d, block, cg, rg, n_cg, n_rg, active, [](double v, int) { return v; }, part, mean);
+    if ((int)threadIdx.x < d) mean[threadIdx.x] = mean[threadIdx.x] / block;
+    __syncthreads();
+    block_sum<T>(xb, d, block, cg, rg, n_cg, n_rg, active,
+                 [&](double v, int c) { const double e = v - mean[c]; return e * e; }, part, var);
+  }
   const int c = threadIdx.x;
   if (c >= d) return;
   const double m = mean[c], s2 = var[c] / block;
