@@ -31,7 +31,8 @@ def rel_err(a, b):
 
 
 @pytest.mark.parametrize("kind,shape,block", [("bf16", (1, 2, 1024, 128), 128), ("f32", (1, 2, 1024, 64), 64),
-                                              ("f64", (2, 1, 256, 16), 32), ("bf16", (1, 1, 512, 168), 16)])
+                                              ("f64", (2, 1, 256, 16), 32), ("bf16", (1, 1, 512, 168), 16),
+                                              ("bf16", (1, 1, 1024, 128), 256)])
 def test_moment_vectors_match_oracle(basa, kind, shape, block):
     note(f"moments {kind} {shape} block {block}")
     g = np.random.Generator(np.random.PCG64(shape[-1] + block))
