@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256, 4) void select_lds_kernel(SelArgs a, int64_t g
 // under the same order, so the result equals the one-pass selection.
 // ---------------------------------------------------------------------------
 constexpr int PART = 512;        // keys per part (KPL 8)
-constexpr int PRW = 2;           // rows per wave in pass 1
+constexpr int PRW = 1;           // rows per wave in pass 1 (one: a shorter chain per wave; 2 rows cost the LoSA step 5 us)
 constexpr int PMAX_K = 256;      // largest top-k of the two-pass path
 
 __host__ __device__ inline int64_t part_count(int64_t n_cand) { return (n_cand + PART - 1) / PART; }
