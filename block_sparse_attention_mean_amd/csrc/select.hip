@@ -805,6 +805,7 @@ hipError_t launch_kr(const SelArgs& a, int64_t batch, hipStream_t s) {
 template <typename T>
 __device__ __forceinline__ double sq_diff_row(const T* cur, const T* prev, int d) {
   double s = 0.0;
+#pragma unroll 8  // the loads of 8 channel groups in flight; the sum keeps its order
   for (int c = 0; c < d; c += 8) {
     float x[8], y[8];
     if constexpr (sizeof(T) == 8) {
