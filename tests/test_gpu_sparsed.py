@@ -40,7 +40,8 @@ def rel_err(a, b):
 
 @pytest.mark.parametrize("kind,hq,hkv,length,d,block", [
     ("f32", 2, 2, 1024, 64, 64), ("bf16", 3, 3, 2048, 128, 128), ("bf16", 4, 2, 1024, 64, 32),
-    ("bf16", 1, 1, 512, 128, 16), ("f32", 1, 1, 256, 8, 4), ("f32", 2, 1, 512, 64, 16)])
+    ("bf16", 1, 1, 512, 128, 16), ("f32", 1, 1, 256, 8, 4), ("f32", 2, 1, 512, 64, 16),
+    ("bf16", 2, 2, 256, 24, 32), ("f32", 1, 1, 128, 8, 16)])
 def test_block_mass_matches_oracle(basa, kind, hq, hkv, length, d, block):
     note(f"block mass {kind} H{hq}/{hkv} L{length} d{d} block{block}")
     g = np.random.Generator(np.random.PCG64(length + d + block))
