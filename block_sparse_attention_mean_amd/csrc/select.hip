@@ -630,10 +630,11 @@ __global__ __launch_bounds__(256, 4) void select_lds_kernel(SelArgs a, int64_t g
 // head (the rows of the query heads of one group, head-major), streams the
 // part's transposed means through LDS in 8-channel chunks (as the LDS-staged
 // kernel does), and writes each row's top-k of the part, in ascending key
-// order, to the workspace (empty slots: candidate -1).  Pass 2: one wave per
-// row takes the top-k of the parts' survivors, which are in ascending key
-// order part after part.  A key in the row's top-k is in its part's top-k
-// under the same order, so the result equals the one-pass selection.
+// order, to the workspace (empty slots: candidate -1).  Pass 2: a workgroup
+// per row takes the top-k of the parts' survivors, which are in ascending key
+// order part after part (in two steps, below).  A key in the row's top-k is in
+// its part's top-k under the same order, so the result equals the one-pass
+// selection.
 // ---------------------------------------------------------------------------
 constexpr int PART = 512;        // keys per part (KPL 8)
 constexpr int PRW = 1;           // rows per wave in pass 1 (one: a shorter chain per wave; 2 rows cost the LoSA step 5 us)
@@ -759,32 +760,79 @@ __global__ __launch_bounds__(256, 2) void select_part_kernel(SelArgs a, int n_pa
   }
 }
 
-template <int KPL2>
-__global__ __launch_bounds__(256) void select_merge_kernel(SelArgs a, int n_parts, int64_t n_rows,
-                                                           const uint64_t* __restrict__ ws_key,
-                                                           const int32_t* __restrict__ ws_cand) {
+// Pass 2, a workgroup per row: wave w takes the top-k of the quarter
+// [w*Q, (w+1)*Q) of the row's n_parts*topk survivors (KPL per lane), and wave 0
+// the top-k of the quarters' survivors (KPL2 per lane), which stay in
+// workspace order, i.e. ascending candidate order.  An entry of the row's top-k
+// is in its quarter's top-k under the same order, so this is exact.  (One wave
+// per row over all survivors took 19 us for the 160 LoSA rows; the four
+// shorter chains take the LoSA step 6 us lower.)
+template <int KPL, int KPL2>
+__global__ __launch_bounds__(256) void select_merge4_kernel(SelArgs a, int n_parts,
+                                                            const uint64_t* __restrict__ ws_key,
+                                                            const int32_t* __restrict__ ws_cand) {
+  __shared__ uint64_t s_key[4][WIDE_MAX_K];
+  __shared__ int32_t s_cand[4][WIDE_MAX_K];
+  __shared__ int s_n[4];
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, h, row) flattened
-  if (r >= n_rows) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = blockIdx.x;  // (b, h, row) flattened
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int n_e = n_parts * a.topk;
-  uint64_t key[KPL2];
-  bool valid[KPL2], sel[KPL2];
-  int cand[KPL2];
+  const int qtr = (n_e + 3) / 4;
+  const int e_lo = wave * qtr, e_hi = min(n_e, e_lo + qtr);
+  uint64_t key[KPL];
+  bool valid[KPL], sel[KPL];
+  int cand[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL2; ++j) {
-    const int e = lane + 64 * j;
-    cand[j] = e < n_e ? ws_cand[r * n_e + e] : -1;
+  for (int j = 0; j < KPL; ++j) {
+    const int e = e_lo + lane + 64 * j;
+    cand[j] = e < e_hi ? ws_cand[r * n_e + e] : -1;
     valid[j] = cand[j] >= 0;
     key[j] = valid[j] ? ws_key[r * n_e + e] : 0ull;
   }
-  wave_topk<KPL2>(key, valid, a.topk, below, sel);
-  int32_t* out = a.idx + r * a.topk;
+  wave_topk<KPL>(key, valid, a.topk, below, sel);
   int base = 0;
 #pragma unroll
-  for (int j = 0; j < KPL2; ++j) {
+  for (int j = 0; j < KPL; ++j) {
     const uint64_t m = __ballot(sel[j]);
-    if (sel[j]) out[base + popc64(m & below)] = cand[j];
+    if (sel[j]) {
+      const int pos = base + popc64(m & below);
+      s_key[wave][pos] = key[j];
+      s_cand[wave][pos] = cand[j];
+    }
+    base += popc64(m);
+  }
+  if (lane == 0) s_n[wave] = base;
+  __syncthreads();
+  if (wave != 0) return;
+  int off[5];
+  off[0] = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) off[w + 1] = off[w] + s_n[w];
+  uint64_t key2[KPL2];
+  bool valid2[KPL2], sel2[KPL2];
+  int cand2[KPL2];
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const int e = lane + 64 * j;
+    valid2[j] = e < off[4];
+    key2[j] = 0ull;
+    cand2[j] = -1;
+    if (valid2[j]) {
+      int w = 0;
+      while (e >= off[w + 1]) ++w;
+      key2[j] = s_key[w][e - off[w]];
+      cand2[j] = s_cand[w][e - off[w]];
+    }
+  }
+  wave_topk<KPL2>(key2, valid2, a.topk, below, sel2);
+  int32_t* out = a.idx + r * a.topk;
+  base = 0;
+#pragma unroll
+  for (int j = 0; j < KPL2; ++j) {
+    const uint64_t m = __ballot(sel2[j]);
+    if (sel2[j]) out[base + popc64(m & below)] = cand2[j];
     base += popc64(m);
   }
 }
@@ -943,11 +991,17 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
     select_part_kernel<<<g1, 256, 0, s>>>(a, n_parts, groups, ws_key, ws_cand);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 g2((unsigned)((n_rows + 3) / 4), 1);
-    if (n_parts * a.topk <= 16 * 64)
-      select_merge_kernel<16><<<g2, 256, 0, s>>>(a, n_parts, n_rows, ws_key, ws_cand);
+    // pass 2: a workgroup per row, quarters of at most 4*64 (or 8*64) survivors
+    dim3 g2((unsigned)n_rows, 1);
+    const int qtr = (n_parts * a.topk + 3) / 4;
+    if (qtr <= 4 * 64 && a.topk <= 128)
+      select_merge4_kernel<4, 8><<<g2, 256, 0, s>>>(a, n_parts, ws_key, ws_cand);
+    else if (qtr <= 4 * 64)
+      select_merge4_kernel<4, 16><<<g2, 256, 0, s>>>(a, n_parts, ws_key, ws_cand);
+    else if (a.topk <= 128)
+      select_merge4_kernel<8, 8><<<g2, 256, 0, s>>>(a, n_parts, ws_key, ws_cand);
     else
-      select_merge_kernel<32><<<g2, 256, 0, s>>>(a, n_parts, n_rows, ws_key, ws_cand);
+      select_merge4_kernel<8, 16><<<g2, 256, 0, s>>>(a, n_parts, ws_key, ws_cand);
     return hipGetLastError();
   }
   if (a.topk <= WIDE_MAX_K) {  // a workgroup per row, four quarters of at most 1024
