@@ -136,6 +136,19 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _shape(name: str, t, want) -> None:
+    """Raise ValueError unless tensor t (when given) has exactly the shape `want`.
+    The C functions receive bare pointers and cannot see sizes, so every
+    tensor is checked here against the sizes passed with it."""
+    if t is not None and tuple(t.shape) != tuple(int(w) for w in want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _int32(name: str, t) -> None:
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -147,26 +160,48 @@ def basa_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None
     outer = 1
     for s in lead:
         outer *= s
+    if block > 0 and length % block == 0:     # otherwise the C call reports BASA_E_SHAPE
+        nb = length // block
+        _shape("mean_rows", mean_rows, (*lead, nb, d))
+        _shape("mean_cols", mean_cols, (*lead, d, nb))
+        _shape("mean_copy", mean_copy, (*lead, nb, d))
     copy_dt = _dt(mean_copy) if mean_copy is not None else F32
     _check("basa_pool", lib.basa_pool(_ptr(x), _dt(x), outer, length, d, block, _ptr(mean_rows),
                                       _ptr(mean_cols), _ptr(mean_copy), copy_dt, _stream()))
 
 
 def _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout):
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, len, head_dim]")
     b, hq, lq, d = q.shape
+    _int32("idx", idx)
+    _int32("q_rows", q_rows)
+    _int32("parent", parent)
     desc = SelectDesc()
     desc.mode = mode
     desc.topk = topk
     desc.batch, desc.heads_q, desc.q_len, desc.head_dim = b, hq, lq, d
     if mode == SELECT_CHANGE:
+        _shape("k", k, q.shape)
+        _shape("idx", idx, (b, topk))
         desc.heads_kv, desc.rows, desc.keys, desc.scale = hq, lq, lq, 1.0
     else:
+        if k.dim() != 4 or idx.dim() != 4:
+            raise ValueError("k must be [batch, heads_kv, head_dim, keys] and idx "
+                             "[batch, heads_q, rows, topk]")
         desc.heads_kv = k.shape[1] if heads_kv is None else heads_kv
         desc.keys = k.shape[-1] if keys is None else keys
         desc.rows = idx.shape[2]
         desc.scale = scale
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
+        _shape("k", k, (b, desc.heads_kv, d, desc.keys))
+        _shape("idx", idx, (b, hq, desc.rows, topk))
+        if q_rows is None and desc.rows != lq:
+            raise ValueError(f"idx has {desc.rows} rows per head but q has {lq} (no q_rows map)")
+        _shape("q_rows", q_rows, (b, desc.rows))
+        if parent is not None:
+            if fanout < 1:
+                raise ValueError("fanout must be >= 1")
+            _shape("parent", parent, (b, hq, (desc.rows + fanout - 1) // fanout, parent.shape[-1]))
     desc.q_rows = _ptr(q_rows)
     desc.parent = _ptr(parent)
     desc.parent_k = parent.shape[-1] if parent is not None else 0
@@ -222,6 +257,8 @@ def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, 
               block_k: int, scale: float, q_rows: torch.Tensor | None = None) -> None:
     """q [B,Hq,Lq,d]; segments from kv_segment(); o [B,Hq,Lq,d]; lse [B,Hq,Lq] float32.
     q_rows [B, lists*tile_q] int32 selects the query rows of each tile."""
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, len, head_dim]")
     b, hq, lq, d = q.shape
     if isinstance(segments, dict):
         segments = [segments]
@@ -229,22 +266,38 @@ def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, 
         raise ValueError("1 to 4 segments")
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
+    if tile_q < 1 or block_k < 1:
+        raise ValueError("tile_q and block_k must be positive")
+    _shape("o", o, q.shape)
+    _shape("lse", lse, (b, hq, lq))
+    _int32("q_rows", q_rows)
+    n_rows = q_rows.shape[-1] if q_rows is not None else lq
+    if n_rows % tile_q:
+        raise ValueError(f"{n_rows} query rows are not a whole number of {tile_q}-row tiles")
+    _shape("q_rows", q_rows, (b, n_rows))
     desc = AttnDesc()
     desc.batch, desc.heads_q, desc.len_q, desc.head_dim = b, hq, lq, d
     desc.heads_kv = segments[0]["k"].shape[1]
-    desc.lists = (q_rows.shape[-1] if q_rows is not None else lq) // tile_q
+    desc.lists = n_rows // tile_q
     desc.tile_q, desc.block_k, desc.n_segments = tile_q, block_k, len(segments)
-    keep = []
     for i, sg in enumerate(segments):
-        if sg["k"].shape[1] != desc.heads_kv:
-            raise ValueError("all segments need the same number of key heads")
+        kk, ix = sg["k"], sg["idx"]
+        if kk.dim() != 4 or kk.shape[0] != b or kk.shape[1] != desc.heads_kv or kk.shape[3] != d:
+            raise ValueError(f"segment {i}: k/v {tuple(kk.shape)} must be [{b}, {desc.heads_kv}, "
+                             f"len, {d}] (all segments share the key heads)")
+        if ix.dim() != 4 or ix.shape[0] != b or ix.shape[1] != hq:
+            raise ValueError(f"segment {i}: idx {tuple(ix.shape)} must be [{b}, {hq}, rows, stride]")
+        if desc.lists and ix.shape[2] <= (desc.lists - 1) >> sg["shift"]:
+            raise ValueError(f"segment {i}: idx has {ix.shape[2]} rows, tile {desc.lists - 1} "
+                             f"reads row {(desc.lists - 1) >> sg['shift']}")
+    for i, sg in enumerate(segments):
+        kk, ix = sg["k"], sg["idx"]
         t = desc.seg[i]
-        t.idx = _ptr(sg["idx"]) + 4 * sg["offset"]
-        t.k, t.v = _ptr(sg["k"]), _ptr(sg["v"])
-        t.len, t.rows = sg["k"].shape[2], sg["idx"].shape[2]
+        t.idx = _ptr(ix) + 4 * sg["offset"]
+        t.k, t.v = _ptr(kk), _ptr(sg["v"])
+        t.len, t.rows = kk.shape[2], ix.shape[2]
         t.count, t.stride, t.shift = sg["count"], sg["stride"], sg["shift"]
-        t.dtype, t.bias = _dt(sg["k"]), sg["bias"]
-        keep.append(sg)
+        t.dtype, t.bias = _dt(kk), sg["bias"]
     desc.q_rows = _ptr(q_rows)
     desc.scale = scale
     _check("basa_attn", lib.basa_attn(ctypes.byref(desc), _ptr(q), _dt(q), _ptr(o), _dt(o),
@@ -255,12 +308,16 @@ def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b:
                o: torch.Tensor, lse: torch.Tensor) -> None:
     """Merge two partials [..., d] + [...] into o, lse (o may be o_a)."""
     d = o_a.shape[-1]
-    rows = o_a.numel() // d
+    rows = o_a.numel() // d if d else 0
     if o_a.dtype != o_b.dtype:
         raise TypeError("partials must share a dtype")
     for t in (lse_a, lse_b, lse):
         if t.dtype != torch.float32:
             raise TypeError("LSE tensors must be float32")
+    _shape("o_b", o_b, o_a.shape)
+    _shape("o", o, o_a.shape)
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse", lse)):
+        _shape(name, t, o_a.shape[:-1])
     _check("basa_merge", lib.basa_merge(rows, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
                                         _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
 
@@ -276,6 +333,9 @@ def basa_pool_moments(x: torch.Tensor, block: int, out: torch.Tensor, role: int,
         outer *= s
     if out.dtype != torch.float64:
         raise TypeError("moments are float64")
+    if block > 0 and length % block == 0:
+        nb = length // block
+        _shape("out", out, (*lead, nb, 3 * d) if role == MOMENTS_QUERY else (*lead, 3 * d, nb))
     _check("basa_pool_moments", lib.basa_pool_moments(_ptr(x), _dt(x), outer, length, d, block, role,
                                                       float(scale), float(beta), _ptr(out), _stream()))
 
@@ -284,11 +344,15 @@ def basa_block_mass(q: torch.Tensor, k: torch.Tensor, block: int, mass: torch.Te
                     scale: float) -> None:
     """mass [B, Hq, Lq/block, Lk/block] float64 <- the dense attention map's
     block mass (rows sum to 1) for q [B, Hq, Lq, d], k [B, Hkv, Lk, d]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, len, head_dim]")
     b, hq, lq, d = q.shape
     if k.dtype != q.dtype or k.shape[0] != b or k.shape[3] != d:
         raise TypeError("q and k must share batch, head_dim and dtype")
     if mass.dtype != torch.float64:
         raise TypeError("mass is float64")
+    if block > 0 and lq % block == 0 and k.shape[2] % block == 0:
+        _shape("mass", mass, (b, hq, lq // block, k.shape[2] // block))
     _check("basa_block_mass", lib.basa_block_mass(_ptr(q), _ptr(k), _dt(q), b, hq, k.shape[1], lq,
                                                   k.shape[2], d, block, float(scale), _ptr(mass),
                                                   _stream()))
@@ -302,6 +366,7 @@ def basa_select_ranges(scores: torch.Tensor, split: int, k_lo: int, k_hi: int,
         raise TypeError("scores are float64 and idx int32")
     n = scores.shape[-1]
     rows = scores.numel() // max(n, 1)
+    _shape("idx", idx, (*scores.shape[:-1], k_lo + k_hi))
     _check("basa_select_ranges", lib.basa_select_ranges(_ptr(scores), rows, n, split, k_lo, k_hi,
                                                         _ptr(idx), _stream()))
 
@@ -315,6 +380,8 @@ def basa_block_radius(x: torch.Tensor, block: int, out: torch.Tensor) -> None:
         outer *= s
     if out.dtype != torch.float64:
         raise TypeError("out is float64")
+    if block > 0 and length % block == 0:
+        _shape("out", out, (*lead, length // block, 2))
     _check("basa_block_radius", lib.basa_block_radius(_ptr(x), _dt(x), outer, length, d, block,
                                                       _ptr(out), _stream()))
 

@@ -21,11 +21,12 @@ __all__ = [
 
 
 def as_f64(x: np.ndarray) -> np.ndarray:
-    """Exact widening to float64; uint16 arrays are read as bf16 bit patterns."""
+    """Exact widening to float64; uint16 arrays are read as bf16 bit patterns.
+    A float64 array is returned as it is (not copied)."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return x.astype(np.float64)
+    return x.astype(np.float64, copy=False)
 
 
 # ---------------------------------------------------------------------------
