@@ -24,7 +24,8 @@ MOMENTS_QUERY, MOMENTS_KEY = 0, 1
 STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE",
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
-EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace", "basa_attn",
+EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace",
+           "basa_select_static", "basa_attn",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
            "basa_block_mass", "basa_select_ranges", "basa_block_radius")
 
@@ -83,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.basa_pool.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i32, vp]
     lib.basa_select.restype = i32
     lib.basa_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
+    lib.basa_select_static.restype = i32
+    lib.basa_select_static.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
     lib.basa_select_workspace.restype = i32
     lib.basa_select_workspace.argtypes = [ctypes.POINTER(SelectDesc), ctypes.POINTER(i64)]
     lib.basa_attn.restype = i32
@@ -224,6 +227,17 @@ def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, 
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     _check("basa_select", lib.basa_select(ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q),
                                           _ptr(idx), _stream()))
+
+
+def basa_select_static(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
+                       mode: int = SELECT_BLOCKS, scale: float = 1.0, heads_kv: int | None = None,
+                       keys: int | None = None, q_rows: torch.Tensor | None = None,
+                       parent: torch.Tensor | None = None, fanout: int = 1) -> None:
+    """basa_select with the library's own device scratch for the two-pass path
+    (no workspace argument, nothing allocated): same tensors and result."""
+    desc = _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout)
+    _check("basa_select_static", lib.basa_select_static(ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q),
+                                                        _ptr(idx), _stream()))
 
 
 def basa_select_workspace(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
@@ -433,7 +447,7 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
                                             mode, _ptr(out), _stream()))
 
 
-__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
+__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
            "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass",

@@ -10,6 +10,7 @@
  *   basa_attn    flash-style attention with an online softmax over the key
  *                blocks listed for each query tile; emits O and the LSE
  *   basa_merge   combines two partial (O, LSE) results of one row
+ *   basa_select_static  basa_select without a caller workspace (no allocation)
  *   basa_pool_moments  block means and variances arranged so that the
  *                covariance-compensated block score is one dot product
  *   basa_block_mass    block mass of the dense attention map
@@ -23,7 +24,8 @@
  * - Every pointer named as device memory must be device memory of the
  *   current HIP device, 16-byte aligned, and stay valid until the work on
  *   `stream` has finished.  The caller owns every buffer; the library never
- *   allocates, frees or keeps device memory.
+ *   allocates or frees device memory.  Its only device memory of its own is
+ *   the fixed scratch array of basa_select_static (one per GPU).
  * - Tensors are dense and row-major in the order their shapes are written.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work and returns; nothing synchronises the host.
@@ -195,6 +197,31 @@ int basa_select(const basa_select_desc* desc, const void* q, const void* k, int 
  * Errors: BASA_E_NULLPTR for a NULL desc or bytes.
  */
 int basa_select_workspace(const basa_select_desc* desc, int64_t* bytes);
+
+/* Size of the device scratch array basa_select_static uses (4 MiB). */
+#define BASA_STATIC_SCRATCH_BYTES (4 << 20)
+
+/*
+ * basa_select_static - basa_select for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the two-pass path uses a 4 MiB device array of this
+ * library instead of a caller-owned workspace.  It calls no allocator.
+ *
+ * Same arguments, results and errors as basa_select, except:
+ *   - desc->workspace must be NULL and desc->workspace_bytes 0
+ *     (BASA_E_UNSUPPORTED otherwise);
+ *   - a request whose two-pass workspace (basa_select_workspace) exceeds
+ *     BASA_STATIC_SCRATCH_BYTES is rejected with BASA_E_SHAPE and nothing is
+ *     launched (e.g. 160 LoSA rows x 4096 keys, top-128, need 1.97 MB);
+ *   - BASA_E_LAUNCH also reports a failure to find the array's device address.
+ * The array exists once per GPU, for the life of the process, and keeps the
+ * last call's contents (every entry a call reads is written earlier in the
+ * same call).  Calls that overlap in time on one GPU (different streams or
+ * host threads) share it and race: serialise them.  The device address is
+ * looked up on the first call on each device, under a lock.
+ */
+int basa_select_static(const basa_select_desc* desc, const void* q, const void* k, int dtype,
+                       int32_t* idx, void* stream);
 
 /* One source of keys for basa_attn.  The key list of query tile t is the
  * concatenation, over the descriptor's segments, of `count` entries of row

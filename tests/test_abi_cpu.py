@@ -100,6 +100,19 @@ def test_select_workspace_size():
     assert basa.lib.basa_select_workspace(ctypes.byref(sel_desc()), None) == NULLPTR
 
 
+def test_select_static_host_checks():
+    # host-only rejections of the no-allocation selection: a caller workspace,
+    # and a two-pass request beyond the library's 4 MiB scratch
+    st = lambda d: basa.lib.basa_select_static(ctypes.byref(d), FAKE, FAKE, basa.F64, FAKE, None)
+    assert basa.lib.basa_select_static(None, FAKE, FAKE, basa.F64, FAKE, None) == NULLPTR
+    assert st(sel_desc(workspace=FAKE, workspace_bytes=1 << 20)) == UNSUPPORTED
+    assert st(sel_desc(workspace_bytes=64)) == UNSUPPORTED
+    big = sel_desc(heads_q=32, heads_kv=8, q_len=16, rows=16, keys=4096, topk=256, head_dim=128,
+                   q_rows=FAKE)
+    assert 32 * 16 * 8 * 256 * 12 > (4 << 20)
+    assert st(big) == SHAPE
+
+
 def test_select_validation():
     assert basa.lib.basa_select(None, FAKE, FAKE, basa.F64, FAKE, None) == NULLPTR
     assert select(sel_desc(topk=0)) == SHAPE
