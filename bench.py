@@ -74,37 +74,114 @@ def attn_traffic(workload: str):
     return m["fetch_bytes"] + m["write_bytes"]
 
 
-def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    pooling + scoring + top-k of one head, then whole query tiles of that head's
-    attention until the time budget is used.  Extrapolated linearly to the whole
-    step and expressed in the same unit as the GPU value."""
-    import oracle as orc
+def wl_bf16_to_f64(a) -> "np.ndarray":
+    """bf16 bit patterns (uint16) or floats -> float64, exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, w, budget_s: float = 15.0) -> dict:
+    """The fp64 C++ oracle (oracle/basa_oracle_ref.cpp, OpenMP over query
+    tiles), as it stands, on a bounded sample of the same workload: pooling +
+    block logits + top-k of head 0, then batches of head 0's query tiles (one
+    tile per thread) until the time budget is used.  Extrapolated linearly to
+    the whole step (all heads, all tiles) and expressed in the GPU value's unit."""
+    import oracle.cref as cref
+    threads = cref.threads()
     h = 0
     t0 = time.perf_counter()
-    qb = orc.pool_mean(x["q"][:, h:h + 1], w.block)
-    kb = orc.pool_mean(x["k"][:, h:h + 1], w.block)
-    idx = orc.topk_ascending(orc.block_logits(qb, kb, w.scale), w.topk)
+    qb = cref.pool_mean(x["q"][:, h:h + 1], w.block)
+    kb = cref.pool_mean(x["k"][:, h:h + 1], w.block)
+    idx = cref.topk_ascending(cref.block_logits(qb, kb, w.scale), w.topk)
     t_sel_head = time.perf_counter() - t0
-    kh, vh = orc.as_f64(x["k"][0, h]), orc.as_f64(x["v"][0, h])
+    # the head's keys and values widened to float64 once (exact), outside the timed loop
+    kh, vh = (np.ascontiguousarray(wl_bf16_to_f64(x[n][:, h:h + 1])) for n in ("k", "v"))
     tiles = 0
     t1 = time.perf_counter()
-    while tiles < 2 or (time.perf_counter() - t1 < budget_s and tiles < w.blocks):
-        rows = x["q"][0, h, tiles * w.block:(tiles + 1) * w.block]
-        orc.attend_rows(rows, kh, vh, idx[0, 0, tiles], w.block, w.scale)
-        tiles += 1
+    while tiles < w.blocks and (tiles == 0 or time.perf_counter() - t1 < budget_s):
+        n = min(threads, w.blocks - tiles)
+        cref.sparse_attention(x["q"][:, h:h + 1, tiles * w.block:(tiles + n) * w.block], kh, vh,
+                              idx[:, :, tiles:tiles + n], w.block, w.block, w.scale)
+        tiles += n
     t_tile = (time.perf_counter() - t1) / tiles
     est = t_sel_head * w.heads + t_tile * w.heads * w.blocks
     flops = 4.0 * w.block ** 3 * w.heads * w.blocks * w.topk
-    return {"value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head 0: pool+score+top-k ({t_sel_head:.2f} s) and {tiles} of {w.blocks} "
-                      f"query tiles of attention ({t_tile:.3f} s each); scaled linearly to "
+    return {"value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu": _cpu_model(),
+            "sample": f"fp64 C++ oracle, {threads} OpenMP threads: head 0 pool+score+top-k "
+                      f"({t_sel_head:.2f} s) and {tiles} of {w.blocks} query tiles of attention "
+                      f"({t_tile * threads:.2f} s per batch of {threads}); scaled linearly to "
                       f"{w.heads} heads (est. {est:.0f} s for the whole step)"}
+
+
+def measured_peaks(torch) -> dict:
+    """Peaks measured on this GPU by the probe kernels of libbasa_peak.so: a
+    bf16 matrix-core loop (8 independent 32x32x16 MFMA chains per wave, two
+    4-wave workgroups per CU: the attention kernel's occupancy, all resident,
+    about 0.15 s per call) and streaming HBM kernels (a 4 GiB read, a 2 GiB
+    copy).  Each figure is the median of three timed calls after one warm-up."""
+    import ctypes
+    import statistics
+    here = os.path.join(ROOT, "block_sparse_attention_mean_amd")
+    lib = ctypes.CDLL(os.path.join(here, "libbasa_peak.so"))
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.peak_mfma_flops.restype = ctypes.c_double
+    lib.peak_mfma_flops.argtypes = [i64, ctypes.c_int]
+    lib.peak_mfma_bf16.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.peak_hbm_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.peak_hbm_copy.argtypes = [vp, vp, i64, i64, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda").manual_seed(5)
+    seed = torch.randn(4160 * 8, device="cuda", generator=g).to(torch.bfloat16)
+    wgs, iters = 512, 500
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=3):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(ts)
+
+    def mfma():
+        assert lib.peak_mfma_bf16(seed.data_ptr(), out.data_ptr(), wgs, iters, stream) == 0
+    t_mfma = timed(mfma)
+    nread = 4 << 30
+    src = torch.empty(nread, dtype=torch.uint8, device="cuda").fill_(7)
+    sums = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+
+    def rd():
+        assert lib.peak_hbm_read(src.data_ptr(), nread, sums.data_ptr(), 8192, stream) == 0
+    t_read = timed(rd)
+    ncopy = 2 << 30
+    dst = torch.empty(ncopy, dtype=torch.uint8, device="cuda")
+
+    def cp():
+        assert lib.peak_hbm_copy(src.data_ptr(), dst.data_ptr(), ncopy, 8192, stream) == 0
+    t_copy = timed(cp)
+    del src, dst, sums, out
+    return {"bf16_mfma_TFLOP/s": lib.peak_mfma_flops(wgs, iters) / t_mfma / 1e12,
+            "hbm_read_GB/s": nread / t_read / 1e9, "hbm_copy_GB/s": 2 * ncopy / t_copy / 1e9,
+            "note": "bf16 MFMA loop at the attention kernel's occupancy; streaming 4 GiB read and "
+                    "2 GiB copy (read + write bytes); medians of 3 calls after a warm-up"}
 
 
 def _time(torch, fn, reps=10):
@@ -230,7 +307,8 @@ def fidelity_stage(torch, wl, basa) -> dict:
 
 def llsa_and_losa_stages(torch, wl, basa) -> dict:
     """The hierarchical (log-linear) forward on the 256x256-image workload and the
-    LoSA prefix step on the 64K-prefix workload."""
+    LoSA prefix step on the 64K-prefix workload, each with its fraction of the
+    HBM peak on algorithmic bytes (the bytes the step cannot avoid moving)."""
     import math
     import block_sparse_attention_mean_amd.pipelines as pl
 
@@ -244,9 +322,18 @@ def llsa_and_losa_stages(torch, wl, basa) -> dict:
     n, h, d = 65536, 4, 64
     keys = 400
     flops = 4.0 * h * n * keys * d
-    out["llsa64k"] = {"ms": t_pool + t_sel + t_attn, "pool_ms": t_pool, "select_ms": t_sel,
+    tensor = h * n * d * 2
+    # Q, K, V read once, O (bf16) and LSE (float32) written once
+    llsa_bytes = 3 * tensor + tensor + h * n * 4
+    t_all = t_pool + t_sel + t_attn
+    out["llsa64k"] = {"ms": t_all, "pool_ms": t_pool, "select_ms": t_sel,
                       "attn_ms": t_attn, "attn_TFLOP/s": flops / (t_attn * 1e-3) / 1e12,
-                      "keys_per_query": keys}
+                      "attn_frac_mfma": flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                      "algorithmic_bytes": llsa_bytes,
+                      "frac_hbm": llsa_bytes / (t_all * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "keys_per_query": keys,
+                      "bound": "latency of the gathered 16-key blocks (400 keys per query, "
+                               "16 queries per tile); neither HBM nor the matrix core is near its peak"}
     y = wl.make_losa(1004)
     hq, t, dd = 32, 16, 128
     cache_o = torch.zeros(1, hq, t, dd, dtype=torch.float32, device="cuda")
@@ -256,7 +343,27 @@ def llsa_and_losa_stages(torch, wl, basa) -> dict:
                     1.0 / math.sqrt(128))
     t_prep = _time(torch, s.prepare)
     t_step = _time(torch, s.step)
+    torch.cuda.synchronize()
+    # algorithmic bytes of a step: the union over each key head's active rows of the kept
+    # prefix blocks (K and V, bf16), the pooled prefix keys read by the selection (float64),
+    # the queries, the block's K/V, and the cache rows and outputs
+    sel = s.sel.cpu().numpy()[0]                      # [Hq, n_active, topk]
+    hkv = y["k_prefix"].shape[1]
+    grp = hq // hkv
+    union = sum(len(np.unique(sel[g * grp:(g + 1) * grp])) for g in range(hkv))
+    union_bytes = union * 16 * dd * 2 * 2
+    kbar_bytes = hkv * (y["k_prefix"].shape[2] // 16) * dd * 8
+    small = 2 * hq * t * dd * 2 + 2 * hkv * t * dd * 2 + 2 * hq * t * (dd * 4 + 4) + hq * t * (dd * 2 + 4)
+    step_bytes = union_bytes + kbar_bytes + small
+    seg = basa.kv_segment(s.sel, s.k_prefix, s.v_prefix)
+    t_prefix = _time(torch, lambda: basa.basa_attn(s.q_cur, seg, s.cache_o, s.cache_lse, tile_q=1,
+                                                   block_k=16, scale=s.scale, q_rows=s.active))
     out["losa64k_step"] = {"ms": t_step, "prefix_pool_ms": t_prep,
+                           "union_blocks": int(union), "union_kv_bytes": union_bytes,
+                           "algorithmic_bytes": step_bytes,
+                           "frac_hbm": step_bytes / (t_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "prefix_attn_ms": t_prefix,
+                           "prefix_attn_frac_hbm": union_bytes / (t_prefix * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "note": "per denoising step: active-token pick, selection, sparse prefix "
                                    "attention for 5 tokens x 32 heads, in-block attention, merge"}
     return out
@@ -334,15 +441,21 @@ def main():
     attn_tflops = flops / (t_attn * 1e-3) / 1e12
     pool_bytes = 2 * (w.heads * w.tokens * w.head_dim * 2) + 2 * (w.heads * nb * w.head_dim * 8)
     sel_bytes = 2 * (w.heads * nb * w.head_dim * 8) + w.heads * nb * w.topk * 4
+    # pool+select, algorithmic: Q and K read once (bf16) + the int32 kept indices written
+    ps_bytes = 2 * (w.heads * w.tokens * w.head_dim * 2) + w.heads * nb * w.topk * 4
 
     stages = {
         "pool_q_k": {"ms": t_pool, "GB/s": pool_bytes / (t_pool * 1e-3) / 1e9,
                      "frac_hbm": pool_bytes / (t_pool * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "select": {"ms": t_sel, "GB/s": sel_bytes / (t_sel * 1e-3) / 1e9,
                    "fp64_GFLOP/s": 2.0 * w.heads * nb * nb * w.head_dim / (t_sel * 1e-3) / 1e9},
-        "pool+select": {"ms": t_ps,
-                        "frac_hbm": (pool_bytes + w.heads * nb * w.topk * 4) / (t_ps * 1e-3)
-                        / 1e9 / PEAK_HBM_GBS},
+        "pool+select": {"ms": t_ps, "algorithmic_bytes": ps_bytes,
+                        "GB/s": ps_bytes / (t_ps * 1e-3) / 1e9,
+                        "frac_hbm": ps_bytes / (t_ps * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "intermediate_bytes": 2 * 2 * (w.heads * nb * w.head_dim * 8),
+                        "note": "algorithmic bytes: Q and K read once, kept indices written; the "
+                                "float64 block means (written by the pooling, read by the "
+                                "selection) are listed apart as intermediate_bytes"},
         "attn": {"ms": t_attn, "TFLOP/s": attn_tflops},
     }
 
@@ -402,8 +515,18 @@ def main():
         "pct_mfma_peak_step": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "stages": stages,
     }
+    if not args.no_stages:
+        peaks = measured_peaks(torch)
+        result["measured_peaks"] = peaks
+        result["roofline"]["peak_measured"] = peaks["bf16_mfma_TFLOP/s"]
+        result["roofline"]["frac_of_measured"] = attn_tflops / peaks["bf16_mfma_TFLOP/s"]
+        for name in ("pool_q_k", "merge"):
+            if name in stages and "GB/s" in stages[name]:
+                stages[name]["frac_of_measured_read"] = stages[name]["GB/s"] / peaks["hbm_read_GB/s"]
+        stages["pool+select"]["frac_of_measured_read"] = (stages["pool+select"]["GB/s"]
+                                                          / peaks["hbm_read_GB/s"])
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (fp64 C++ oracle, bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(result))
 

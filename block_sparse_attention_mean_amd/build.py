@@ -15,6 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbasa.so")
+PEAK_SRC = os.path.join(HERE, "probes", "peak.hip")
+PEAK_LIB = os.path.join(HERE, "libbasa_peak.so")   # measured-peak kernels for bench.py only
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code: the compiler
@@ -61,7 +63,21 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_peak(verbose)
     return LIB
+
+
+def build_peak(verbose: bool = False) -> str:
+    """Compile the measured-peak kernels (probes/peak.hip) into libbasa_peak.so."""
+    tmp = PEAK_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", PEAK_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAK_SRC}:\n{res.stderr}")
+    os.replace(tmp, PEAK_LIB)
+    return PEAK_LIB
 
 
 if __name__ == "__main__":

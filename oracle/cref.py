@@ -16,12 +16,13 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "basa_oracle_ref.cpp")
 LIB = os.path.join(HERE, "liboracle_ref.so")
+GXX_FLAGS = ["-O2", "-std=c++17", "-fopenmp", "-shared", "-fPIC"]
 
 
 def build() -> str:
-    """Compile the reference with g++ (plain -O2, no fast-math) into oracle/liboracle_ref.so."""
+    """Compile the reference with g++ (plain -O2, no fast-math, OpenMP) into oracle/liboracle_ref.so."""
     tmp = LIB + ".tmp"
-    subprocess.run(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", SRC, "-o", tmp], check=True)
+    subprocess.run(["g++", *GXX_FLAGS, SRC, "-o", tmp], check=True)
     os.replace(tmp, LIB)
     return LIB
 
@@ -37,8 +38,15 @@ def _load() -> ctypes.CDLL:
     lib.oracle_sparse_attention.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p, i64, i64, i64,
                                             f64, p, p]
     lib.oracle_merge.argtypes = [p, p, p, p, i64, i64, p, p]
+    lib.oracle_llsa_num_levels.argtypes = [i64, i64]
+    lib.oracle_llsa_num_levels.restype = i64
+    lib.oracle_llsa_forward.argtypes = [p, p, p, i64, i64, i64, i64, i64, f64, i64, p, p, p]
+    lib.oracle_losa_step.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64,
+                                     i64, f64, p, p, p, p, p, p, p, p]
+    lib.oracle_threads.argtypes = []
     for f in (lib.oracle_pool_mean, lib.oracle_block_logits, lib.oracle_topk,
-              lib.oracle_sparse_attention, lib.oracle_merge):
+              lib.oracle_sparse_attention, lib.oracle_merge, lib.oracle_llsa_forward,
+              lib.oracle_losa_step, lib.oracle_threads):
         f.restype = ctypes.c_int
     return lib
 
@@ -120,3 +128,57 @@ def merge(o_a, lse_a, o_b, lse_b):
     _ok(_l().oracle_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), rows, d, _ptr(o), _ptr(lse)),
         "merge")
     return o, lse
+
+
+def threads() -> int:
+    """Threads the reference's OpenMP loops use."""
+    return int(_l().oracle_threads())
+
+
+def llsa_num_levels(n: int, block: int) -> int:
+    lv = int(_l().oracle_llsa_num_levels(n, block))
+    if lv < 0:
+        raise ValueError(f"sequence length {n} is not a multiple of block {block}")
+    return lv
+
+
+def llsa_forward(q, k, v, block: int, topk: int, scale: float, levels: int | None = None):
+    """q, k, v [H, N, d] -> {"sel": {l: [H, N/block^l, topk]}, "o", "lse", "levels"}."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    h, n, d = q.shape
+    if levels is None:
+        levels = llsa_num_levels(n, block)
+    sizes = [n // block ** lv for lv in range(levels + 1)]
+    sel = np.empty(sum(h * sizes[lv] * topk for lv in range(1, levels + 1)), dtype=np.int32)
+    o = np.empty((h, n, v.shape[-1]))
+    lse = np.empty((h, n))
+    _ok(_l().oracle_llsa_forward(_ptr(q), _ptr(k), _ptr(v), h, n, d, block, topk, scale, levels,
+                                 _ptr(sel), _ptr(o), _ptr(lse)), "llsa_forward")
+    out, off = {}, 0
+    for lv in range(1, levels + 1):
+        m = h * sizes[lv] * topk
+        out[lv] = sel[off:off + m].reshape(h, sizes[lv], topk)
+        off += m
+    return {"sel": out, "o": o, "lse": lse, "levels": levels, "sizes": sizes}
+
+
+def losa_step(q_cur, q_prev, k_prefix, v_prefix, k_block, v_block, cache_o, cache_lse,
+              n_active: int, block: int, topk: int, scale: float):
+    """The LoSA denoising step; same inputs and result keys as the numpy oracle's losa_step."""
+    qc, qp = _f64(q_cur), _f64(q_prev)
+    kp, vp = _f64(k_prefix), _f64(v_prefix)
+    kb, vb = _f64(k_block), _f64(v_block)
+    co, cl = _f64(cache_o), _f64(cache_lse)
+    b, hq, t, d = qc.shape
+    hkv, p = kp.shape[1], kp.shape[2]
+    act = np.empty((b, n_active), dtype=np.int32)
+    sel = np.empty((b, hq, n_active, topk), dtype=np.int32)
+    nco, ncl = np.empty(co.shape), np.empty(cl.shape)
+    o_in, lse_in = np.empty(co.shape), np.empty(cl.shape)
+    o, lse = np.empty(co.shape), np.empty(cl.shape)
+    _ok(_l().oracle_losa_step(_ptr(qc), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(kb), _ptr(vb), _ptr(co),
+                              _ptr(cl), b, hq, hkv, t, p, d, n_active, block, topk, scale, _ptr(act),
+                              _ptr(sel), _ptr(nco), _ptr(ncl), _ptr(o_in), _ptr(lse_in), _ptr(o),
+                              _ptr(lse)), "losa_step")
+    return {"active": act, "sel": sel, "o": o, "lse": lse, "cache_o": nco, "cache_lse": ncl,
+            "o_in": o_in, "lse_in": lse_in}

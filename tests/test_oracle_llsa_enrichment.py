@@ -20,15 +20,25 @@ computable by hand:
    differ from group to group; O and LSE are closed forms per group, and a
    value shift planted in a coarse token that only one group's candidate set
    holds moves that group's rows by its exact weight.
+
+Every pin runs on both references: the numpy oracle and the C++ one.
 """
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle as orc
+import oracle.cref as cref
 
 LN16 = math.log(16.0)
+
+
+@pytest.fixture(params=["numpy", "cpp"])
+def llsa(request):
+    """llsa_forward of the numpy oracle or of the C++ reference (same result keys)."""
+    return orc.llsa_forward if request.param == "numpy" else cref.llsa_forward
 
 
 def _sdpa(q, k, v, scale):
@@ -44,11 +54,11 @@ def _avgpool16(x):
     return torch.nn.functional.avg_pool1d(t, 16, 16).transpose(-1, -2).numpy()
 
 
-def test_one_level_nothing_pruned_equals_sdpa_over_repeated_means():
+def test_one_level_nothing_pruned_equals_sdpa_over_repeated_means(llsa):
     g = np.random.Generator(np.random.PCG64(101))
     h, n, d, scale = 2, 256, 8, 0.4
     q, k, v = (g.standard_normal((h, n, d)) for _ in range(3))
-    res = orc.llsa_forward(q, k, v, 16, 16, scale)
+    res = llsa(q, k, v, 16, 16, scale)
     assert res["levels"] == 1
     assert np.array_equal(res["sel"][1][0, 0], np.arange(16))          # every level-1 token kept
     kc = np.repeat(_avgpool16(k), 16, axis=1)                           # 16 copies of each mean
@@ -58,13 +68,13 @@ def test_one_level_nothing_pruned_equals_sdpa_over_repeated_means():
     assert np.abs(res["lse"] - lse_ref).max() < 1e-12
 
 
-def test_two_levels_all_ties_closed_form():
+def test_two_levels_all_ties_closed_form(llsa):
     g = np.random.Generator(np.random.PCG64(103))
     n, d = 4096, 8
     q = g.standard_normal((1, n, d))
     k = np.zeros((1, n, d))
     v = g.standard_normal((1, n, d))
-    res = orc.llsa_forward(q, k, v, 16, 8, 0.3)
+    res = llsa(q, k, v, 16, 8, 0.3)
     assert res["levels"] == 2
     # ties go to the lower index: level 2 keeps tokens 0..7 of 16, level 1 keeps
     # 0..7 of its candidates 0..127; fine keys are tokens 0..127
@@ -96,10 +106,10 @@ def _others(p):
     return [c for c in range(16) if c != p][:7]
 
 
-def test_two_levels_group_candidate_sets_closed_form():
+def test_two_levels_group_candidate_sets_closed_form(llsa):
     scale = 0.25
     q, k, v = _aligned()
-    res = orc.llsa_forward(q, k, v, 16, 8, scale)
+    res = llsa(q, k, v, 16, 8, scale)
     assert res["levels"] == 2
     big = math.exp(scale * 2.0 * 2.0)              # e^(scale * alpha * beta)
     vv = v[0]
@@ -121,7 +131,7 @@ def test_two_levels_group_candidate_sets_closed_form():
         assert np.abs(res["o"][0, rows] - num / z).max() < 1e-12, p
 
 
-def test_coarse_value_shift_moves_only_its_candidate_group():
+def test_coarse_value_shift_moves_only_its_candidate_group(llsa):
     """Level-1 token c = 16*10 + 12 is a candidate only of group 10 (no other
     level-2 query keeps block 10) and is not among the fine keys (group 10
     keeps children 160..167).  Shifting the values of its 16 fine tokens by D
@@ -130,11 +140,11 @@ def test_coarse_value_shift_moves_only_its_candidate_group():
     256 e^E in group 10)."""
     scale = 0.25
     q, k, v = _aligned(seed=109)
-    base = orc.llsa_forward(q, k, v, 16, 8, scale)
+    base = llsa(q, k, v, 16, 8, scale)
     c, shift = 16 * 10 + 12, np.linspace(-1.0, 1.0, 16)
     v2 = v.copy()
     v2[0, 16 * c:16 * (c + 1)] += shift
-    moved = orc.llsa_forward(q, k, v2, 16, 8, scale)
+    moved = llsa(q, k, v2, 16, 8, scale)
     big = math.exp(scale * 4.0)
     w_lse = np.exp(base["lse"][0])                  # LSE does not depend on values
     assert np.array_equal(moved["lse"], base["lse"])
