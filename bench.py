@@ -356,14 +356,21 @@ def llsa_and_losa_stages(torch, wl, basa) -> dict:
     small = 2 * hq * t * dd * 2 + 2 * hkv * t * dd * 2 + 2 * hq * t * (dd * 4 + 4) + hq * t * (dd * 2 + 4)
     step_bytes = union_bytes + kbar_bytes + small
     seg = basa.kv_segment(s.sel, s.k_prefix, s.v_prefix)
-    t_prefix = _time(torch, lambda: basa.basa_attn(s.q_cur, seg, s.cache_o, s.cache_lse, tile_q=1,
-                                                   block_k=16, scale=s.scale, q_rows=s.active))
+    kw = dict(tile_q=1, block_k=16, scale=s.scale, q_rows=s.active)
+    t_prefix = _time(torch, basa.prepare_attn(s.q_cur, seg, s.cache_o, s.cache_lse, **kw))
+    # the same prefix attention as one walk over each key head's union of kept blocks
+    ws = torch.empty(basa.basa_attn_workspace(s.q_cur, seg, s.cache_o, s.cache_lse, **kw),
+                     dtype=torch.uint8, device="cuda")
+    t_union = _time(torch, basa.prepare_attn(s.q_cur, seg, s.cache_o, s.cache_lse, workspace=ws, **kw))
     out["losa64k_step"] = {"ms": t_step, "prefix_pool_ms": t_prep,
                            "union_blocks": int(union), "union_kv_bytes": union_bytes,
                            "algorithmic_bytes": step_bytes,
                            "frac_hbm": step_bytes / (t_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "prefix_attn_ms": t_prefix,
                            "prefix_attn_frac_hbm": union_bytes / (t_prefix * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "prefix_attn_union_walk_ms": t_union,
+                           "prefix_attn_union_walk_frac_hbm": union_bytes / (t_union * 1e-3) / 1e9
+                           / PEAK_HBM_GBS,
                            "note": "per denoising step: active-token pick, selection, sparse prefix "
                                    "attention for 5 tokens x 32 heads, in-block attention, merge"}
     return out

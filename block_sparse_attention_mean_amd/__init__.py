@@ -25,7 +25,7 @@ STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace",
-           "basa_select_static", "basa_attn",
+           "basa_select_static", "basa_attn", "basa_attn_workspace",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
            "basa_block_mass", "basa_select_ranges", "basa_block_radius")
 
@@ -67,6 +67,7 @@ class AttnDesc(ctypes.Structure):
         ("tile_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("n_segments", ctypes.c_int32),
         ("reserved", ctypes.c_int32), ("seg", KvSegment * MAX_SEGMENTS),
         ("q_rows", ctypes.c_void_p), ("scale", ctypes.c_double),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -88,6 +89,8 @@ def _load() -> ctypes.CDLL:
     lib.basa_select_static.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
     lib.basa_select_workspace.restype = i32
     lib.basa_select_workspace.argtypes = [ctypes.POINTER(SelectDesc), ctypes.POINTER(i64)]
+    lib.basa_attn_workspace.restype = i32
+    lib.basa_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(i64)]
     lib.basa_attn.restype = i32
     lib.basa_attn.argtypes = [ctypes.POINTER(AttnDesc), vp, i32, vp, i32, vp, vp]
     lib.basa_merge.restype = i32
@@ -159,6 +162,12 @@ def _stream() -> int:
 def basa_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None,
               mean_cols: torch.Tensor | None = None, mean_copy: torch.Tensor | None = None) -> None:
     """Block means of x [..., len, head_dim] into the given float64/float32/bf16 outputs."""
+    prepare_pool(x, block, mean_rows, mean_cols, mean_copy)()
+
+
+def prepare_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None,
+                 mean_cols: torch.Tensor | None = None, mean_copy: torch.Tensor | None = None):
+    """basa_pool validated once; the returned function issues it on torch's current stream."""
     *lead, length, d = x.shape
     outer = 1
     for s in lead:
@@ -169,8 +178,18 @@ def basa_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = None
         _shape("mean_cols", mean_cols, (*lead, d, nb))
         _shape("mean_copy", mean_copy, (*lead, nb, d))
     copy_dt = _dt(mean_copy) if mean_copy is not None else F32
-    _check("basa_pool", lib.basa_pool(_ptr(x), _dt(x), outer, length, d, block, _ptr(mean_rows),
-                                      _ptr(mean_cols), _ptr(mean_copy), copy_dt, _stream()))
+    args = (_ptr(x), _dt(x), outer, length, d, block, _ptr(mean_rows), _ptr(mean_cols),
+            _ptr(mean_copy), copy_dt)
+    return _prepared("basa_pool", lib.basa_pool, args, (x, mean_rows, mean_cols, mean_copy))
+
+
+def _prepared(name, fn, args, keep):
+    """A function that calls fn(*args, stream) on torch's current stream and checks the status;
+    `keep` holds the objects the pointers in args belong to."""
+    def call():
+        _check(name, fn(*args, torch.cuda.current_stream().cuda_stream))
+    call.keep = keep
+    return call
 
 
 def _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout):
@@ -221,12 +240,23 @@ def basa_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, 
     idx [B,Hq,rows,topk] int32.  CHANGE: q, k [B,H,T,d] current/previous queries,
     idx [B,topk] int32.  workspace: optional device scratch (uint8), see
     basa_select_workspace."""
+    prepare_select(q, k, idx, topk, mode=mode, scale=scale, heads_kv=heads_kv, keys=keys,
+                   q_rows=q_rows, parent=parent, fanout=fanout, workspace=workspace)()
+
+
+def prepare_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
+                   mode: int = SELECT_BLOCKS, scale: float = 1.0, heads_kv: int | None = None,
+                   keys: int | None = None, q_rows: torch.Tensor | None = None,
+                   parent: torch.Tensor | None = None, fanout: int = 1,
+                   workspace: torch.Tensor | None = None):
+    """basa_select validated once; the returned function issues it on torch's current stream."""
     desc = _select_desc(q, k, idx, topk, mode, scale, heads_kv, keys, q_rows, parent, fanout)
     if workspace is not None:
         desc.workspace = _ptr(workspace)
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
-    _check("basa_select", lib.basa_select(ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q),
-                                          _ptr(idx), _stream()))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q), _ptr(idx))
+    return _prepared("basa_select", lib.basa_select, args,
+                     (desc, q, k, idx, q_rows, parent, workspace))
 
 
 def basa_select_static(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
@@ -267,10 +297,8 @@ def kv_segment(idx: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, count: in
             "shift": shift, "bias": bias}
 
 
-def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, tile_q: int,
-              block_k: int, scale: float, q_rows: torch.Tensor | None = None) -> None:
-    """q [B,Hq,Lq,d]; segments from kv_segment(); o [B,Hq,Lq,d]; lse [B,Hq,Lq] float32.
-    q_rows [B, lists*tile_q] int32 selects the query rows of each tile."""
+def _attn_desc(q, segments, o, lse, tile_q, block_k, scale, q_rows, workspace):
+    """Validated AttnDesc for basa_attn (every shape checked before any pointer is taken)."""
     if q.dim() != 4:
         raise ValueError("q must be [batch, heads, len, head_dim]")
     b, hq, lq, d = q.shape
@@ -289,6 +317,8 @@ def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, 
     if n_rows % tile_q:
         raise ValueError(f"{n_rows} query rows are not a whole number of {tile_q}-row tiles")
     _shape("q_rows", q_rows, (b, n_rows))
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
     desc = AttnDesc()
     desc.batch, desc.heads_q, desc.len_q, desc.head_dim = b, hq, lq, d
     desc.heads_kv = segments[0]["k"].shape[1]
@@ -314,13 +344,53 @@ def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, 
         t.dtype, t.bias = _dt(kk), sg["bias"]
     desc.q_rows = _ptr(q_rows)
     desc.scale = scale
-    _check("basa_attn", lib.basa_attn(ctypes.byref(desc), _ptr(q), _dt(q), _ptr(o), _dt(o),
-                                      _ptr(lse), _stream()))
+    if workspace is not None:
+        desc.workspace = _ptr(workspace)
+        desc.workspace_bytes = workspace.numel()
+    return desc
+
+
+def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, tile_q: int,
+              block_k: int, scale: float, q_rows: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> None:
+    """q [B,Hq,Lq,d]; segments from kv_segment(); o [B,Hq,Lq,d]; lse [B,Hq,Lq] float32.
+    q_rows [B, lists*tile_q] int32 selects the query rows of each tile.  workspace:
+    optional uint8 device scratch (see basa_attn_workspace)."""
+    prepare_attn(q, segments, o, lse, tile_q=tile_q, block_k=block_k, scale=scale, q_rows=q_rows,
+                 workspace=workspace)()
+
+
+def basa_attn_workspace(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *,
+                        tile_q: int, block_k: int, scale: float,
+                        q_rows: torch.Tensor | None = None) -> int:
+    """Bytes of workspace that let basa_attn walk the union of the rows' blocks (0: none)."""
+    desc = _attn_desc(q, segments, o, lse, tile_q, block_k, scale, q_rows, None)
+    out = ctypes.c_int64(0)
+    _check("basa_attn_workspace", lib.basa_attn_workspace(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def prepare_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, tile_q: int,
+                 block_k: int, scale: float, q_rows: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """Validate a basa_attn call once and return a function that issues it on
+    torch's current stream (for loops that repeat the same call on the same
+    buffers: the descriptor and pointers are built here, not per call).  The
+    tensors must stay alive and keep their storage while the function is used."""
+    desc = _attn_desc(q, segments, o, lse, tile_q, block_k, scale, q_rows, workspace)
+    args = (ctypes.byref(desc), _ptr(q), _dt(q), _ptr(o), _dt(o), _ptr(lse))
+    return _prepared("basa_attn", lib.basa_attn, args, (desc, q, segments, o, lse, q_rows, workspace))
 
 
 def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
                o: torch.Tensor, lse: torch.Tensor) -> None:
     """Merge two partials [..., d] + [...] into o, lse (o may be o_a)."""
+    prepare_merge(o_a, lse_a, o_b, lse_b, o, lse)()
+
+
+def prepare_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                  o: torch.Tensor, lse: torch.Tensor):
+    """basa_merge validated once; the returned function issues it on torch's current stream."""
     d = o_a.shape[-1]
     rows = o_a.numel() // d if d else 0
     if o_a.dtype != o_b.dtype:
@@ -332,8 +402,9 @@ def basa_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b:
     _shape("o", o, o_a.shape)
     for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse", lse)):
         _shape(name, t, o_a.shape[:-1])
-    _check("basa_merge", lib.basa_merge(rows, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
-                                        _dt(o_a), _ptr(o), _dt(o), _ptr(lse), _stream()))
+    args = (rows, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _dt(o_a), _ptr(o), _dt(o),
+            _ptr(lse))
+    return _prepared("basa_merge", lib.basa_merge, args, (o_a, lse_a, o_b, lse_b, o, lse))
 
 
 def basa_pool_moments(x: torch.Tensor, block: int, out: torch.Tensor, role: int,
@@ -447,7 +518,8 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
                                             mode, _ptr(out), _stream()))
 
 
-__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn", "basa_merge", "kv_segment", "BasaError", "lib",
+__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn",
+           "basa_attn_workspace", "prepare_attn", "prepare_pool", "prepare_select", "prepare_merge", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
            "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass",

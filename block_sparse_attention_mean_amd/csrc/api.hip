@@ -161,6 +161,8 @@ int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (basa::attn_mfma_supported(d, q_dtype, o_dtype))
       return from_hip(basa::launch_attn_mfma(d, q, o, o_dtype, lse, s));
+    if (d->workspace && aligned16(d->workspace) && basa::attn_union_supported(d, d->workspace_bytes))
+      return from_hip(basa::launch_attn_union(d, q, q_dtype, o, o_dtype, lse, d->workspace, s));
     if (basa::attn_row_supported(d))
       return from_hip(basa::launch_attn_row(d, q, q_dtype, o, o_dtype, lse, s));
     if (basa::attn_t16_supported(d, q_dtype))
@@ -168,6 +170,16 @@ int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int 
     if (basa::attn_tile_supported(d))
       return from_hip(basa::launch_attn_tile(d, q, q_dtype, o, o_dtype, lse, s));
     return from_hip(basa::launch_attn_generic(d, q, q_dtype, o, o_dtype, lse, s));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_attn_workspace(const basa_attn_desc* d, int64_t* bytes) {
+  try {
+    if (!d || !bytes) return BASA_E_NULLPTR;
+    *bytes = basa::attn_union_workspace_bytes(d);
+    return BASA_OK;
   } catch (...) {
     return BASA_E_LAUNCH;
   }

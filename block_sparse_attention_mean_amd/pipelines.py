@@ -27,9 +27,10 @@ import math
 import torch
 
 from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS,
-               SELECT_CHANGE, basa_attn, basa_block_mass, basa_merge, basa_permute, basa_pool,
-               basa_pool_moments, basa_rank, basa_rank_workspace, basa_select, basa_select_ranges,
-               basa_select_workspace, kv_segment)
+               SELECT_CHANGE, basa_attn, basa_attn_workspace, basa_block_mass, basa_merge,
+               basa_permute, basa_pool, basa_pool_moments, basa_rank, basa_rank_workspace,
+               basa_select, basa_select_ranges, basa_select_workspace, kv_segment, prepare_attn,
+               prepare_merge, prepare_pool, prepare_select)
 
 
 def _empty(*shape, dtype, like):
@@ -297,10 +298,17 @@ class LosaStep:
     cache_lse [B, Hq, T] float32 are updated in place for the active rows.
     prepare() pools the prefix keys (once per generation block); step() runs
     the per-step work and fills self.active, self.sel, self.o (bf16), self.lse.
+    The step's six calls are validated once, here; step() only issues them.
+    union_walk: give the prefix attention its workspace, so that each key
+    head's union of kept blocks is read once.  The default (False) lets every
+    row walk its own list: on the 64K-prefix workload that takes 29 us against
+    44 us for the union walk (both are bound by the latency of their block
+    chains; blocks that several rows keep are found in the cache).
     """
 
     def __init__(self, q_cur, q_prev, k_prefix, v_prefix, k_block, v_block, cache_o, cache_lse,
-                 n_active: int = 5, block: int = 16, topk: int = 128, scale: float | None = None):
+                 n_active: int = 5, block: int = 16, topk: int = 128, scale: float | None = None,
+                 union_walk: bool = False):
         b, hq, t, d = q_cur.shape
         self.q_cur, self.q_prev = q_cur, q_prev
         self.k_prefix, self.v_prefix = k_prefix, v_prefix
@@ -321,20 +329,29 @@ class LosaStep:
         # scratch of the prefix selection (lets it run in two passes over 512-key parts)
         n_ws = basa_select_workspace(self.q64, self.kbt, self.sel, topk, q_rows=self.active)
         self.ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q_cur.device) if n_ws else None
+        # scratch of the prefix attention (lets it walk each key head's union of kept blocks once)
+        prefix = kv_segment(self.sel, self.k_prefix, self.v_prefix)
+        kw = dict(tile_q=1, block_k=self.block, scale=self.scale, q_rows=self.active)
+        n_aws = basa_attn_workspace(self.q_cur, prefix, self.cache_o, self.cache_lse, **kw)
+        self.attn_ws = (torch.empty(n_aws, dtype=torch.uint8, device=q_cur.device)
+                        if n_aws and union_walk else None)
+        # the step's calls, validated once (their buffers never change)
+        self.calls = [
+            prepare_select(self.q_cur, self.q_prev, self.active, self.n_active, mode=SELECT_CHANGE),
+            prepare_pool(self.q_cur, 1, mean_rows=self.q64),
+            prepare_select(self.q64, self.kbt, self.sel, self.topk, scale=self.scale,
+                           q_rows=self.active, workspace=self.ws),
+            prepare_attn(self.q_cur, prefix, self.cache_o, self.cache_lse, workspace=self.attn_ws,
+                         **kw),
+            prepare_attn(self.q_cur, kv_segment(self.inblock, self.k_block, self.v_block), self.o_in,
+                         self.lse_in, tile_q=t, block_k=t, scale=self.scale),
+            prepare_merge(self.cache_o, self.cache_lse, self.o_in, self.lse_in, self.o, self.lse),
+        ]
 
     def prepare(self):
         basa_pool(self.k_prefix, self.block, mean_cols=self.kbt)
 
     def step(self):
-        t = self.q_cur.shape[2]
-        basa_select(self.q_cur, self.q_prev, self.active, self.n_active, mode=SELECT_CHANGE)
-        basa_pool(self.q_cur, 1, mean_rows=self.q64)
-        basa_select(self.q64, self.kbt, self.sel, self.topk, scale=self.scale,
-                    q_rows=self.active, workspace=self.ws)
-        basa_attn(self.q_cur, kv_segment(self.sel, self.k_prefix, self.v_prefix), self.cache_o,
-                  self.cache_lse, tile_q=1, block_k=self.block, scale=self.scale,
-                  q_rows=self.active)
-        basa_attn(self.q_cur, kv_segment(self.inblock, self.k_block, self.v_block), self.o_in,
-                  self.lse_in, tile_q=t, block_k=t, scale=self.scale)
-        basa_merge(self.cache_o, self.cache_lse, self.o_in, self.lse_in, self.o, self.lse)
+        for call in self.calls:
+            call()
         return self.o, self.lse

@@ -263,6 +263,16 @@ typedef struct basa_attn_desc {
      and other rows of o and lse are left untouched (the LoSA cache update). */
   const int32_t* q_rows;
   double scale;       /* logit scale, normally 1/sqrt(head_dim) */
+  /* optional device scratch, owned by the caller (NULL: none).  With at
+     least basa_attn_workspace() bytes, rows given by a row map (tile_q 1,
+     one bf16 segment of 16-key blocks, at most 32 rows per key head) are
+     computed as one walk over the union of each key head's kept blocks:
+     every block of the union is read once (the LoSA step's active rows).
+     Without it each row walks its own list; the result is the same up to
+     float32 rounding.  The call overwrites it; calls that overlap in time
+     must not share it. */
+  void* workspace;
+  int64_t workspace_bytes;
 } basa_attn_desc;
 
 /*
@@ -290,6 +300,21 @@ typedef struct basa_attn_desc {
  */
 int basa_attn(const basa_attn_desc* desc, const void* q, int q_dtype, void* o, int o_dtype,
               float* lse, void* stream);
+
+/*
+ * basa_attn_workspace - bytes of workspace that let basa_attn take the
+ * union walk for this request (0: the request never uses one).  Reads only
+ * the sizes and types in desc.  The union walk follows the LoSA post
+ * ("KV inflation" and method steps 2-4): the active rows of one key head
+ * each keep their own prefix blocks, and the data the step must move is the
+ * union of those selections.  The prefix blocks of a key head are cut into
+ * chunks of 64 blocks; each chunk's union is read once and every row that
+ * kept a block attends to it, giving per-(chunk, row) partial results
+ * (unnormalised O, max, sum: (head_dim + 2) floats each) in the workspace,
+ * which a second kernel combines per row by the online-softmax merge rule.
+ * Errors: BASA_E_NULLPTR for a NULL desc or bytes.
+ */
+int basa_attn_workspace(const basa_attn_desc* desc, int64_t* bytes);
 
 /*
  * basa_merge - combine two partial attention results of the same rows.
