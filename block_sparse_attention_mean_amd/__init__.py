@@ -25,7 +25,8 @@ STATUS = {0: "BASA_OK", 1: "BASA_E_NULLPTR", 2: "BASA_E_SHAPE", 3: "BASA_E_DTYPE
           4: "BASA_E_ALIGN", 5: "BASA_E_UNSUPPORTED", 6: "BASA_E_LAUNCH"}
 
 EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "basa_select_workspace",
-           "basa_select_static", "basa_attn", "basa_attn_workspace",
+           "basa_select_static", "basa_pool_select", "basa_pool_select_workspace", "basa_attn",
+           "basa_attn_workspace",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
            "basa_block_mass", "basa_select_ranges", "basa_block_radius")
 
@@ -85,6 +86,10 @@ def _load() -> ctypes.CDLL:
     lib.basa_pool.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i32, vp]
     lib.basa_select.restype = i32
     lib.basa_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
+    lib.basa_pool_select.restype = i32
+    lib.basa_pool_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, i64, vp, vp, vp, vp]
+    lib.basa_pool_select_workspace.restype = i32
+    lib.basa_pool_select_workspace.argtypes = [ctypes.POINTER(SelectDesc), ctypes.POINTER(i64)]
     lib.basa_select_static.restype = i32
     lib.basa_select_static.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
     lib.basa_select_workspace.restype = i32
@@ -257,6 +262,63 @@ def prepare_select(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: in
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q), _ptr(idx))
     return _prepared("basa_select", lib.basa_select, args,
                      (desc, q, k, idx, q_rows, parent, workspace))
+
+
+def _pool_select_desc(q, k, qbar, kbar_t, idx, topk, block, scale):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, len, head_dim]")
+    b, hq, lq, d = q.shape
+    if k.shape[0] != b or k.shape[3] != d or k.dtype != q.dtype:
+        raise ValueError("k must share batch, head_dim and dtype with q")
+    hkv, lk = k.shape[1], k.shape[2]
+    if block < 1 or lq % block or lk % block:
+        raise ValueError(f"lengths {lq}, {lk} are not multiples of block {block}")
+    nq, nk = lq // block, lk // block
+    _int32("idx", idx)
+    _shape("qbar", qbar, (b, hq, nq, d))
+    _shape("kbar_t", kbar_t, (b, hkv, d, nk))
+    _shape("idx", idx, (b, hq, nq, topk))
+    if qbar.dtype != torch.float64 or kbar_t.dtype != torch.float64:
+        raise TypeError("qbar and kbar_t are float64")
+    desc = SelectDesc()
+    desc.mode, desc.topk = SELECT_BLOCKS, topk
+    desc.batch, desc.heads_q, desc.heads_kv = b, hq, hkv
+    desc.q_len, desc.rows, desc.keys, desc.head_dim, desc.scale = nq, nq, nk, d, scale
+    return desc
+
+
+def basa_pool_select_workspace(q: torch.Tensor, k: torch.Tensor, qbar: torch.Tensor,
+                               kbar_t: torch.Tensor, idx: torch.Tensor, topk: int, *, block: int,
+                               scale: float = 1.0) -> int:
+    """Bytes of workspace (counters) basa_pool_select uses for its single-launch form."""
+    desc = _pool_select_desc(q, k, qbar, kbar_t, idx, topk, block, scale)
+    out = ctypes.c_int64(0)
+    _check("basa_pool_select_workspace", lib.basa_pool_select_workspace(ctypes.byref(desc),
+                                                                        ctypes.byref(out)))
+    return out.value
+
+
+def prepare_pool_select(q: torch.Tensor, k: torch.Tensor, qbar: torch.Tensor, kbar_t: torch.Tensor,
+                        idx: torch.Tensor, topk: int, *, block: int, scale: float = 1.0,
+                        workspace: torch.Tensor | None = None):
+    """basa_pool_select validated once: q [B,Hq,Lq,d], k [B,Hkv,Lk,d] -> qbar [B,Hq,Lq/block,d],
+    kbar_t [B,Hkv,d,Lk/block] (float64), idx [B,Hq,Lq/block,topk] (int32)."""
+    desc = _pool_select_desc(q, k, qbar, kbar_t, idx, topk, block, scale)
+    if workspace is not None:
+        desc.workspace = _ptr(workspace)
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _dt(q), block, _ptr(qbar), _ptr(kbar_t), _ptr(idx))
+    return _prepared("basa_pool_select", lib.basa_pool_select, args,
+                     (desc, q, k, qbar, kbar_t, idx, workspace))
+
+
+def basa_pool_select(q: torch.Tensor, k: torch.Tensor, qbar: torch.Tensor, kbar_t: torch.Tensor,
+                     idx: torch.Tensor, topk: int, *, block: int, scale: float = 1.0,
+                     workspace: torch.Tensor | None = None) -> None:
+    """Pool q (rows) and k (transposed) by `block` and select each query block's top-k key
+    blocks, as basa_pool + basa_pool + basa_select; one persistent launch when it applies."""
+    prepare_pool_select(q, k, qbar, kbar_t, idx, topk, block=block, scale=scale,
+                        workspace=workspace)()
 
 
 def basa_select_static(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, topk: int, *,
@@ -519,6 +581,7 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
 
 
 __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn",
+           "basa_pool_select", "basa_pool_select_workspace", "prepare_pool_select",
            "basa_attn_workspace", "prepare_attn", "prepare_pool", "prepare_select", "prepare_merge", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",

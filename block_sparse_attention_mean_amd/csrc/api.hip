@@ -118,6 +118,48 @@ int basa_select(const basa_select_desc* d, const void* q, const void* k, int dty
   }
 }
 
+int basa_pool_select(const basa_select_desc* d, const void* q, const void* k, int dtype,
+                     int64_t block, double* qbar, double* kbar_t, int32_t* idx, void* stream) {
+  try {
+    if (!d) return BASA_E_NULLPTR;
+    if (d->mode != BASA_SELECT_BLOCKS || d->q_rows || d->parent) return BASA_E_UNSUPPORTED;
+    if (dtype != BASA_F32 && dtype != BASA_BF16 && dtype != BASA_F64) return BASA_E_DTYPE;
+    if (block < 1 || d->batch < 0 || d->heads_q < 1 || d->q_len < 0 || d->topk < 1)
+      return BASA_E_SHAPE;
+    if (d->head_dim < 8 || d->head_dim > 512 || d->head_dim % 8 != 0) return BASA_E_SHAPE;
+    if (d->heads_kv < 1 || d->heads_q % d->heads_kv != 0) return BASA_E_SHAPE;
+    if (d->rows != d->q_len || d->keys < 1 || d->keys > 4096 || d->topk > d->keys) return BASA_E_SHAPE;
+    if (!(d->scale > 0.0) || !std::isfinite(d->scale)) return BASA_E_SHAPE;
+    if (d->q_len > INT64_MAX / block || d->keys > INT64_MAX / block) return BASA_E_SHAPE;
+    if (d->batch == 0 || d->q_len == 0) return BASA_OK;
+    if (!q || !k || !qbar || !kbar_t || !idx) return BASA_E_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(qbar) || !aligned16(kbar_t)) return BASA_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (basa::pool_select_fused(d, dtype, block))
+      return from_hip(basa::launch_pool_select(d, q, k, block, qbar, kbar_t, idx, s));
+    // the same three steps as separate launches
+    hipError_t e = basa::launch_pool(q, dtype, d->batch * d->heads_q, d->q_len * block, d->head_dim,
+                                     block, qbar, nullptr, nullptr, BASA_F32, s);
+    if (e != hipSuccess) return BASA_E_LAUNCH;
+    e = basa::launch_pool(k, dtype, d->batch * d->heads_kv, d->keys * block, d->head_dim, block,
+                          nullptr, kbar_t, nullptr, BASA_F32, s);
+    if (e != hipSuccess) return BASA_E_LAUNCH;
+    return from_hip(basa::launch_select_blocks(d, qbar, kbar_t, idx, s));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_pool_select_workspace(const basa_select_desc* d, int64_t* bytes) {
+  try {
+    if (!d || !bytes) return BASA_E_NULLPTR;
+    *bytes = basa::pool_select_workspace_bytes(d);
+    return BASA_OK;
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_select_workspace(const basa_select_desc* d, int64_t* bytes) {
   try {
     if (!d || !bytes) return BASA_E_NULLPTR;

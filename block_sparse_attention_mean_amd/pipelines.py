@@ -68,12 +68,17 @@ class BaForward:
         self.idx = _empty(b, h, nb, topk, dtype=torch.int32, like=q)
         self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
         self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
+        self._select = None
+        if beta is None:
+            # the selection stage's three calls, validated once
+            self._select = [prepare_pool(q, block, mean_rows=self.qbar),
+                            prepare_pool(k, block, mean_cols=self.kbt),
+                            prepare_select(self.qbar, self.kbt, self.idx, topk, scale=self.scale)]
 
     def select(self):
         if self.beta is None:
-            basa_pool(self.q, self.block, mean_rows=self.qbar)
-            basa_pool(self.k, self.block, mean_cols=self.kbt)
-            basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=self.scale)
+            for call in self._select:
+                call()
             return
         basa_pool_moments(self.q, self.block, self.qbar, MOMENTS_QUERY, self.scale, self.beta)
         basa_pool_moments(self.k, self.block, self.kbt, MOMENTS_KEY, 1.0, self.beta)

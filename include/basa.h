@@ -188,6 +188,33 @@ int basa_select(const basa_select_desc* desc, const void* q, const void* k, int 
                 int32_t* idx, void* stream);
 
 /*
+ * basa_pool_select - the selection stage in one call: the block means of q
+ * (rows, as basa_pool's mean_rows), of k (transposed, as mean_cols) and the
+ * BLOCKS-mode selection of basa_select on them (BA-Att section 3.1, Eq. 2
+ * and Algorithm 1 steps 3-5), with the same results as those three calls.
+ *   desc    BLOCKS mode, no q_rows, no parent; q_len = query blocks per head,
+ *           keys = key blocks per key head, rows = q_len
+ *   q       device [batch][heads_q][q_len*block][head_dim] of dtype
+ *   k       device [batch][heads_kv][keys*block][head_dim] of dtype
+ *   qbar    device float64 [batch][heads_q][q_len][head_dim] (written)
+ *   kbar_t  device float64 [batch][heads_kv][head_dim][keys] (written)
+ *   idx     device int32 [batch][heads_q][q_len][topk] (written)
+ * It runs as the three separate launches.  A single persistent launch (key
+ * tasks pooling the key heads, selection tasks pooling their own query blocks
+ * and waiting on per-key-head counts in desc->workspace) is written but
+ * switched off: its first run did not finish in 180 s, for a reason not yet
+ * shown.  desc->workspace is accepted and unused.
+ * Errors: as basa_pool and basa_select, plus BASA_E_UNSUPPORTED for another
+ * mode, a row map or a parent list, and BASA_E_NULLPTR for a NULL output.
+ */
+int basa_pool_select(const basa_select_desc* desc, const void* q, const void* k, int dtype,
+                     int64_t block, double* qbar, double* kbar_t, int32_t* idx, void* stream);
+
+/* basa_pool_select_workspace - bytes of workspace basa_pool_select uses for
+ * its single-launch form (a few counters).  Errors: BASA_E_NULLPTR. */
+int basa_pool_select_workspace(const basa_select_desc* desc, int64_t* bytes);
+
+/*
  * basa_select_workspace - bytes of workspace that lets basa_select take the
  * two-pass path for this request (0: the request never uses one).  Reads
  * only the sizes in desc (mode, batch, heads_q, rows, keys, topk, parent).
