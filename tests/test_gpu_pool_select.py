@@ -32,7 +32,7 @@ def _bf16(g, *shape):
     return wl.f32_to_bf16(g.standard_normal(shape, dtype=np.float32))
 
 
-def _run(basa, q, k, block, topk, scale, use_ws=True, reps=2):
+def _run(basa, q, k, block, topk, scale, use_ws=True, reps=2, single_launch=False):
     qt, kt = dev(q), dev(k)
     b, hq, lq, d = qt.shape
     hkv, lk = kt.shape[1], kt.shape[2]
@@ -48,7 +48,9 @@ def _run(basa, q, k, block, topk, scale, use_ws=True, reps=2):
         basa.basa_pool_select(qt, kt, qbar, kbt, idx, topk, block=block, scale=scale, workspace=ws)
         torch.cuda.synchronize()
         outs.append((host(qbar), host(kbt), host(idx)))
-    flag = int(ws.view(torch.int32)[1].item()) if ws is not None else 0
+    # the wait-bound flag exists only in the single launch's workspace; the
+    # separate launches leave the workspace as the caller filled it
+    flag = int(ws.view(torch.int32)[1].item()) if single_launch else 0
     # the separate calls
     qb2 = torch.empty_like(qbar)
     kb2 = torch.empty_like(kbt)
@@ -74,7 +76,7 @@ def test_pool_select_dlm64k(basa):
     note("pool_select dlm64k: H32 L65536 block128 top128, one launch")
     w = wl.WORKLOADS["dlm64k"]
     x = wl.generate("dlm64k")
-    outs, sep, flag = _run(basa, x["q"], x["k"], w.block, w.topk, w.scale)
+    outs, sep, flag = _run(basa, x["q"], x["k"], w.block, w.topk, w.scale, single_launch=True)
     ref = orc.topk_ascending(orc.block_logits(orc.pool_mean(x["q"], w.block),
                                               orc.pool_mean(x["k"], w.block), w.scale), w.topk)
     _check(outs, sep, flag, ref)
