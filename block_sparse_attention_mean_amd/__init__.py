@@ -425,7 +425,8 @@ def basa_attn(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *, 
 def basa_attn_workspace(q: torch.Tensor, segments, o: torch.Tensor, lse: torch.Tensor, *,
                         tile_q: int, block_k: int, scale: float,
                         q_rows: torch.Tensor | None = None) -> int:
-    """Bytes of workspace that let basa_attn walk the union of the rows' blocks (0: none)."""
+    """Bytes of workspace basa_attn can use for this request (0: none): the union walk of
+    row-mapped 16-key rows, or the query-tile order of the bf16 128-row MFMA path."""
     desc = _attn_desc(q, segments, o, lse, tile_q, block_k, scale, q_rows, None)
     out = ctypes.c_int64(0)
     _check("basa_attn_workspace", lib.basa_attn_workspace(ctypes.byref(desc), ctypes.byref(out)))

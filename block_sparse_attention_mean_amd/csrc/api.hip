@@ -201,8 +201,13 @@ int basa_attn(const basa_attn_desc* d, const void* q, int q_dtype, void* o, int 
       if (!aligned16(g.k) || !aligned16(g.v)) return BASA_E_ALIGN;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (basa::attn_mfma_supported(d, q_dtype, o_dtype))
-      return from_hip(basa::launch_attn_mfma(d, q, o, o_dtype, lse, s));
+    if (basa::attn_mfma_supported(d, q_dtype, o_dtype)) {
+      const int64_t need = basa::attn_mfma_workspace_bytes(d);
+      int32_t* order = need > 0 && d->workspace && aligned16(d->workspace) && d->workspace_bytes >= need
+                           ? static_cast<int32_t*>(d->workspace)
+                           : nullptr;
+      return from_hip(basa::launch_attn_mfma(d, q, o, o_dtype, lse, order, s));
+    }
     if (d->workspace && aligned16(d->workspace) && basa::attn_union_supported(d, d->workspace_bytes))
       return from_hip(basa::launch_attn_union(d, q, q_dtype, o, o_dtype, lse, d->workspace, s));
     if (basa::attn_row_supported(d))
@@ -221,6 +226,9 @@ int basa_attn_workspace(const basa_attn_desc* d, int64_t* bytes) {
   try {
     if (!d || !bytes) return BASA_E_NULLPTR;
     *bytes = basa::attn_union_workspace_bytes(d);
+    if (*bytes == 0 && d->n_segments >= 1 && d->n_segments <= BASA_MAX_SEGMENTS &&
+        basa::attn_mfma_supported(d, BASA_BF16, BASA_BF16))
+      *bytes = basa::attn_mfma_workspace_bytes(d);
     return BASA_OK;
   } catch (...) {
     return BASA_E_LAUNCH;

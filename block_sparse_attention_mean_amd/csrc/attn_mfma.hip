@@ -55,7 +55,13 @@
 // Tiles are numbered so that in every round of 8 x 64 resident workgroups all
 // XCDs work on one contiguous run of tiles (the same head), each XCD on its
 // own contiguous sub-run: the head's K/V stays in the shared last-level cache
-// and neighbouring query tiles, whose kept blocks overlap, share an L2.
+// and query tiles whose kept blocks overlap share an L2.  With a workspace,
+// the tiles of each (batch, head) are first ranked by the middle entry of
+// their lists (tile_order_kernel) and a sub-run takes consecutive ranks: the
+// 64 tiles that walk their ascending lists side by side on one XCD then sit
+// near the same key blocks at the same time, and fewer blocks leave the L2
+// before their last reader.  Each tile is computed the same way wherever it
+// runs, so the order changes no output bit.
 #include "common.h"
 
 namespace basa {
@@ -93,6 +99,7 @@ struct MfmaArgs {
   int64_t len_q, len_k, lists, tiles, idx_rows;
   int heads_q, heads_kv, group, kept, idx_stride;
   float scale_log2;
+  const int32_t* order;  // [batch*heads_q][lists] tile ranks, or null (natural order)
 };
 
 __device__ __forceinline__ int swap_bits_2_3(int x) {
@@ -256,7 +263,8 @@ __device__ __forceinline__ void stage(const Walk& w, int i, const bf16x8* qf, co
 
 template <bool OUT_BF16, bool REG>
 __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
-  const int64_t tile = tile_of(blockIdx.x, a.tiles);
+  int64_t tile = tile_of(blockIdx.x, a.tiles);
+  if (a.order) tile = tile / a.lists * a.lists + a.order[tile];
   const int64_t t = tile % a.lists;
   const int64_t bh = tile / a.lists;
   const int h = (int)(bh % a.heads_q);
@@ -391,7 +399,38 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
   if (w.hi == 0) a.lse[orow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+constexpr int ORDER_MAX = 2048;  // lists per head that tile_order_kernel ranks (keys in LDS)
+
+// order[bh][r] = the tile of (batch, head) bh with rank r by the middle entry
+// of its list (ties by tile index); entries outside the key range rank as 0.
+// One workgroup per (batch, head); ranks by counting, lists <= ORDER_MAX.
+__global__ __launch_bounds__(256) void tile_order_kernel(MfmaArgs a, int nblk_k, int32_t* order) {
+  __shared__ int32_t key[ORDER_MAX];
+  const int64_t bh = blockIdx.x;
+  const int n = (int)a.lists;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int32_t k = a.kv_idx[(bh * a.idx_rows + t) * a.idx_stride + a.kept / 2];
+    key[t] = (k >= 0 && k < nblk_k) ? k : 0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int kt = key[t];
+    int r = 0;
+    for (int u = 0; u < n; ++u) {
+      const int ku = key[u];
+      r += (ku < kt) | ((ku == kt) & (u < t));
+    }
+    order[bh * n + r] = t;
+  }
+}
+
 }  // namespace
+
+int64_t attn_mfma_workspace_bytes(const basa_attn_desc* d) {
+  const basa_kv_segment& g = d->seg[0];
+  if (d->lists < 1 || d->lists > ORDER_MAX || g.count < 1 || d->batch < 1) return 0;
+  return (d->batch * d->heads_q * d->lists * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
+}
 
 bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype) {
   const basa_kv_segment& g = d->seg[0];
@@ -403,7 +442,7 @@ bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype) {
 }
 
 hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int o_dtype,
-                            float* lse, hipStream_t s) {
+                            float* lse, int32_t* order, hipStream_t s) {
   const basa_kv_segment& g = d->seg[0];
   MfmaArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -423,7 +462,14 @@ hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int
   a.group = (int)(d->heads_q / d->heads_kv);
   a.kept = g.count;
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
+  a.order = nullptr;
   if (a.tiles == 0) return hipSuccess;
+  if (order) {  // the caller checked the workspace against attn_mfma_workspace_bytes
+    tile_order_kernel<<<dim3((unsigned)(a.tiles / a.lists)), 256, 0, s>>>(a, (int)(a.len_k / BK), order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.order = order;
+  }
   dim3 grid((unsigned)a.tiles);
   const bool reg = g.count <= REG_KEPT;
   if (o_dtype == BASA_BF16) {

@@ -86,8 +86,10 @@ hipError_t launch_pool_select(const basa_select_desc* d, const void* q, const vo
 hipError_t launch_select_change(const basa_select_desc* d, const void* q, const void* k,
                                 int dtype, int32_t* idx, hipStream_t s);
 bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype);
+// order: attn_mfma_workspace_bytes() of device scratch for the tile ranks, or null
+int64_t attn_mfma_workspace_bytes(const basa_attn_desc* d);
 hipError_t launch_attn_mfma(const basa_attn_desc* d, const void* q, void* o, int o_dtype,
-                            float* lse, hipStream_t s);
+                            float* lse, int32_t* order, hipStream_t s);
 int64_t attn_union_workspace_bytes(const basa_attn_desc* d);
 bool attn_union_supported(const basa_attn_desc* d, int64_t workspace_bytes);
 hipError_t launch_attn_union(const basa_attn_desc* d, const void* q, int q_dtype, void* o,

@@ -74,6 +74,13 @@ class BaForward:
             self._select = [prepare_pool(q, block, mean_rows=self.qbar),
                             prepare_pool(k, block, mean_cols=self.kbt),
                             prepare_select(self.qbar, self.kbt, self.idx, topk, scale=self.scale)]
+        # the attention call, validated once, with the workspace in which the
+        # library orders the query tiles (the same output without it)
+        seg = kv_segment(self.idx, k, v)
+        kw = dict(tile_q=block, block_k=block, scale=self.scale)
+        n_ws = basa_attn_workspace(q, seg, self.o, self.lse, **kw)
+        self.attn_ws = _empty(n_ws, dtype=torch.uint8, like=q) if n_ws > 0 else None
+        self._attend = prepare_attn(q, seg, self.o, self.lse, workspace=self.attn_ws, **kw)
 
     def select(self):
         if self.beta is None:
@@ -85,8 +92,7 @@ class BaForward:
         basa_select(self.qbar, self.kbt, self.idx, self.topk, scale=1.0)
 
     def attend(self):
-        basa_attn(self.q, kv_segment(self.idx, self.k, self.v), self.o, self.lse,
-                  tile_q=self.block, block_k=self.block, scale=self.scale)
+        self._attend()
 
     def run(self):
         self.select()
@@ -189,6 +195,7 @@ class SparsedForward:
         self.idx = _empty(b, h, nq, self.k_lo + self.k_hi, dtype=torch.int32, like=q)
         self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
         self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
+        self.attn_ws = None  # tile-order workspace of the attention, sized at the first attend()
 
     def pattern(self):
         basa_block_mass(self.q, self.k, self.block, self.mass, self.scale)
@@ -198,8 +205,12 @@ class SparsedForward:
         q = self.q if q is None else q
         k = self.k if k is None else k
         v = self.v if v is None else v
-        basa_attn(q, kv_segment(self.idx, k, v), self.o, self.lse, tile_q=self.block,
-                  block_k=self.block, scale=self.scale)
+        seg = kv_segment(self.idx, k, v)
+        kw = dict(tile_q=self.block, block_k=self.block, scale=self.scale)
+        if self.attn_ws is None:
+            n_ws = basa_attn_workspace(q, seg, self.o, self.lse, **kw)
+            self.attn_ws = _empty(max(n_ws, 1), dtype=torch.uint8, like=q)
+        basa_attn(q, seg, self.o, self.lse, workspace=self.attn_ws, **kw)
 
     def run(self):
         self.pattern()

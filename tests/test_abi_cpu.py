@@ -187,6 +187,26 @@ def test_attn_validation():
     assert attn(attn_desc(batch=0)) == OK
 
 
+def attn_workspace(desc):
+    out = ctypes.c_int64(-1)
+    assert basa.lib.basa_attn_workspace(ctypes.byref(desc), ctypes.byref(out)) == OK
+    return out.value
+
+
+def test_attn_workspace_sizes():
+    # the MFMA path (bf16, head_dim 128, 128-row tiles of 128-key blocks, one
+    # segment) takes one int32 tile rank per query tile, rounded up to 256 bytes
+    assert attn_workspace(attn_desc()) == 256                      # 1 x 4 heads x 2 tiles
+    assert attn_workspace(attn_desc(batch=3, heads_q=8, heads_kv=8, lists=100, len_q=12800,
+                                    seg_rows=100)) == (3 * 8 * 100 * 4 + 255) // 256 * 256
+    assert attn_workspace(attn_desc(lists=2049, len_q=2049 * 128, seg_rows=2049)) == 0
+    assert attn_workspace(attn_desc(seg_count=0)) == 0
+    assert attn_workspace(attn_desc(tile_q=64, lists=4)) == 0       # not the MFMA path
+    assert attn_workspace(attn_desc(head_dim=64)) == 0
+    assert attn_workspace(attn_desc(n_seg=2)) == 0
+    assert basa.lib.basa_attn_workspace(None, ctypes.byref(ctypes.c_int64())) == NULLPTR
+
+
 def merge(rows=8, d=128, oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, idt=basa.F32, o=FAKE,
           odt=basa.BF16, lse=FAKE):
     return basa.lib.basa_merge(rows, d, oa, la, ob, lb, idt, o, odt, lse, None)

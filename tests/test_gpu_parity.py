@@ -226,16 +226,25 @@ def test_select_dlm16k_full(basa):
 
 # --------------------------------------------------------------------------- attention
 
-def run_attn(basa, q, segs, tile_q, block_k, scale, o_dtype, q_rows=None, o_init=None, lse_init=None):
-    """segs: list of (idx np, k np, v np, kwargs)."""
+def run_attn(basa, q, segs, tile_q, block_k, scale, o_dtype, q_rows=None, o_init=None, lse_init=None,
+             workspace=False):
+    """segs: list of (idx np, k np, v np, kwargs).  workspace: pass the one
+    basa_attn_workspace asks for (filled with 0x5A, not zeroed)."""
     qt = dev(q)
     segments = [basa.kv_segment(dev(i), dev(k), dev(v), **kw) for i, k, v, kw in segs]
     o = (dev(o_init) if o_init is not None else
          torch.zeros(qt.shape, dtype=o_dtype, device="cuda"))
     lse = (dev(lse_init) if lse_init is not None else
            torch.zeros(qt.shape[:3], dtype=torch.float32, device="cuda"))
-    basa.basa_attn(qt, segments, o, lse, tile_q=tile_q, block_k=block_k, scale=scale,
-                   q_rows=dev(q_rows) if q_rows is not None else None)
+    rows = dev(q_rows) if q_rows is not None else None
+    ws = None
+    if workspace:
+        n = basa.basa_attn_workspace(qt, segments, o, lse, tile_q=tile_q, block_k=block_k, scale=scale,
+                                     q_rows=rows)
+        assert n > 0
+        ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    basa.basa_attn(qt, segments, o, lse, tile_q=tile_q, block_k=block_k, scale=scale, q_rows=rows,
+                   workspace=ws)
     torch.cuda.synchronize()
     return host(o), host(lse)
 
@@ -343,6 +352,37 @@ def test_attn_mfma_dlm16k_stratified_and_deterministic(basa):
     eo, el = check_tiles_against_oracle(o, lse, x["q"], x["k"], x["v"], idx, tiles, 128, 128, w.scale)
     note(f"dlm16k 512 tiles: O err {eo:.2e}, LSE err {el:.2e}")
     assert eo <= O_TOL and el <= LSE_TOL
+
+
+@pytest.mark.parametrize("case", ["batch2_gqa_padded", "odd_lists", "dlm16k"])
+def test_attn_mfma_tile_order_changes_no_bit(basa, case):
+    # With a workspace the MFMA path ranks each head's query tiles by the middle
+    # entry of their lists and runs them in that order; each tile is computed
+    # the same way wherever it runs, so O and LSE must match the natural order
+    # bit for bit (lists with -1 slots, a -1 at the middle slot, an unsorted
+    # list, an odd number of tiles per head, and the 16K workload's lists).
+    note(f"attn mfma tile order: {case}, with and without the workspace")
+    scale = 1 / math.sqrt(128)
+    g = np.random.Generator(np.random.PCG64(31))
+    if case == "dlm16k":
+        w = wl.WORKLOADS["dlm16k"]
+        x = wl.generate("dlm16k")
+        q, k, v = x["q"], x["k"], x["v"]
+        idx = oracle_select(q, k, w.block, w.topk, w.scale)
+        scale = w.scale
+    else:
+        b, hq, hkv, nb, kept = (2, 4, 2, 8, 3) if case == "batch2_gqa_padded" else (1, 3, 3, 9, 5)
+        q = wl.f32_to_bf16(g.standard_normal((b, hq, nb * 128, 128)).astype(np.float32))
+        k = wl.f32_to_bf16(g.standard_normal((b, hkv, nb * 128, 128)).astype(np.float32))
+        v = wl.f32_to_bf16(g.standard_normal((b, hkv, nb * 128, 128)).astype(np.float32))
+        idx = np.sort(g.random((b, hq, nb, nb)).argsort(-1)[..., :kept], axis=-1).astype(np.int32)
+        idx[0, 1, 2, kept // 2] = -1                        # the ranking key slot is empty
+        idx[-1, -1, -1, 0] = -1
+        idx[0, 0, 1] = idx[0, 0, 1][::-1]                   # a list in descending order
+    o1, l1 = run_attn(basa, q, [(idx, k, v, {})], 128, 128, scale, torch.bfloat16)
+    o2, l2 = run_attn(basa, q, [(idx, k, v, {})], 128, 128, scale, torch.bfloat16, workspace=True)
+    assert np.isfinite(o1).all() and np.isfinite(l1).all()   # no list is empty here
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)  # host() widens exactly
 
 
 def test_attn_generic_tiny_fp32(basa):
