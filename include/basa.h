@@ -290,14 +290,18 @@ typedef struct basa_attn_desc {
      and other rows of o and lse are left untouched (the LoSA cache update). */
   const int32_t* q_rows;
   double scale;       /* logit scale, normally 1/sqrt(head_dim) */
-  /* optional device scratch, owned by the caller (NULL: none).  With at
-     least basa_attn_workspace() bytes, rows given by a row map (tile_q 1,
-     one bf16 segment of 16-key blocks, at most 32 rows per key head) are
-     computed as one walk over the union of each key head's kept blocks:
-     every block of the union is read once (the LoSA step's active rows).
-     Without it each row walks its own list; the result is the same up to
-     float32 rounding.  The call overwrites it; calls that overlap in time
-     must not share it. */
+  /* optional device scratch, owned by the caller (NULL: none), 16-byte
+     aligned.  With at least basa_attn_workspace() bytes:
+     - rows given by a row map (tile_q 1, one bf16 segment of 16-key blocks,
+       at most 32 rows per key head) are computed as one walk over the union
+       of each key head's kept blocks: every block of the union is read once
+       (the LoSA step's active rows).  Without it each row walks its own
+       list; the result is the same up to float32 rounding.
+     - on the MFMA path (see basa_attn) the query tiles of each (batch,
+       head) are ranked by the middle entry of their lists and run in that
+       order, so that tiles running side by side on one XCD keep nearby key
+       blocks and share its L2.  The output is bit-identical without it.
+     The call overwrites it; calls that overlap in time must not share it. */
   void* workspace;
   int64_t workspace_bytes;
 } basa_attn_desc;
@@ -329,9 +333,13 @@ int basa_attn(const basa_attn_desc* desc, const void* q, int q_dtype, void* o, i
               float* lse, void* stream);
 
 /*
- * basa_attn_workspace - bytes of workspace that let basa_attn take the
- * union walk for this request (0: the request never uses one).  Reads only
- * the sizes and types in desc.  The union walk follows the LoSA post
+ * basa_attn_workspace - bytes of workspace basa_attn can use for this request
+ * (0: the request never uses one).  Reads only the sizes and types in desc.
+ * MFMA-path requests (bf16, head_dim 128, 128-row tiles of 128-key blocks,
+ * one segment, at most 2048 tiles per head) take one int32 rank per query
+ * tile (batch * heads_q * lists * 4 bytes, rounded up to 256) for the tile
+ * order described at basa_attn_desc.workspace.  Row-map requests of 16-key
+ * blocks take the union walk's partials, below.  The union walk follows the LoSA post
  * ("KV inflation" and method steps 2-4): the active rows of one key head
  * each keep their own prefix blocks, and the data the step must move is the
  * union of those selections.  The prefix blocks of a key head are cut into
