@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # FETCH_SIZE and WRITE_SIZE (separate runs), each scaled by the same counter on a 1 GiB
 # device copy (factors 2.0 and 1.0); see profiles/attn_mfma_dlm64k.md.  Valid only for
 # the kernel source it was measured on (first 16 hex digits of its sha256).
-MEASURED_ATTN_TRAFFIC = {"source_sha256": "789418d3b06499cb", "fetch_bytes": 53.010e9, "write_bytes": 0.546e9}
+MEASURED_ATTN_TRAFFIC = {"source_sha256": "444d31f91ea40271", "fetch_bytes": 27.525e9, "write_bytes": 0.547e9}
 
 
 def parse():

@@ -400,25 +400,35 @@ __global__ __launch_bounds__(NT, 2) void attn_mfma_kernel(MfmaArgs a) {
 }
 
 constexpr int ORDER_MAX = 2048;  // lists per head that tile_order_kernel ranks (keys in LDS)
+constexpr int ORDER_KEYS = 1 << 20;  // key blocks per head it handles (key * ORDER_MAX + tile < 2^31)
 
 // order[bh][r] = the tile of (batch, head) bh with rank r by the middle entry
 // of its list (ties by tile index); entries outside the key range rank as 0.
-// One workgroup per (batch, head); ranks by counting, lists <= ORDER_MAX.
+// One workgroup per (batch, head).  Each tile's rank is the count of packed
+// keys (middle entry * ORDER_MAX + tile, all distinct) below its own, read
+// four at a time from LDS.
 __global__ __launch_bounds__(256) void tile_order_kernel(MfmaArgs a, int nblk_k, int32_t* order) {
-  __shared__ int32_t key[ORDER_MAX];
+  __shared__ __attribute__((aligned(16))) int32_t key[ORDER_MAX];
   const int64_t bh = blockIdx.x;
   const int n = (int)a.lists;
-  for (int t = threadIdx.x; t < n; t += 256) {
-    const int32_t k = a.kv_idx[(bh * a.idx_rows + t) * a.idx_stride + a.kept / 2];
-    key[t] = (k >= 0 && k < nblk_k) ? k : 0;
+  const int n4 = (n + 3) >> 2;
+  for (int t = threadIdx.x; t < 4 * n4; t += 256) {
+    int32_t packed = INT32_MAX;  // padding to a multiple of 4 ranks above every tile
+    if (t < n) {
+      const int32_t k = a.kv_idx[(bh * a.idx_rows + t) * a.idx_stride + a.kept / 2];
+      packed = ((k >= 0 && k < nblk_k) ? k : 0) * ORDER_MAX + t;
+    }
+    key[t] = packed;
   }
   __syncthreads();
+  const int4* key4 = reinterpret_cast<const int4*>(key);
   for (int t = threadIdx.x; t < n; t += 256) {
     const int kt = key[t];
     int r = 0;
-    for (int u = 0; u < n; ++u) {
-      const int ku = key[u];
-      r += (ku < kt) | ((ku == kt) & (u < t));
+#pragma unroll 4
+    for (int u = 0; u < n4; ++u) {
+      const int4 k4 = key4[u];
+      r += (k4.x < kt) + (k4.y < kt) + (k4.z < kt) + (k4.w < kt);
     }
     order[bh * n + r] = t;
   }
@@ -428,7 +438,8 @@ __global__ __launch_bounds__(256) void tile_order_kernel(MfmaArgs a, int nblk_k,
 
 int64_t attn_mfma_workspace_bytes(const basa_attn_desc* d) {
   const basa_kv_segment& g = d->seg[0];
-  if (d->lists < 1 || d->lists > ORDER_MAX || g.count < 1 || d->batch < 1) return 0;
+  if (d->lists < 1 || d->lists > ORDER_MAX || g.count < 1 || d->batch < 1 || g.len / BK > ORDER_KEYS)
+    return 0;
   return (d->batch * d->heads_q * d->lists * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
 }
 
