@@ -19,6 +19,13 @@
 // The next step's key and value rows are loaded while the current one is being
 // reduced.  At the end the 16 states of a wave are merged with a butterfly and
 // the NW wave states through LDS, with the max-shifted rule of basa_merge.
+//
+// Workgroup numbering: dispatch hands workgroups to the 8 XCDs round-robin, and
+// the rows of one key head (query heads of a group x lists) are consecutive.
+// Rows are cut into chunks of up to 64 consecutive rows and chunk c runs on XCD
+// c % 8, so the rows of one key head share one L2 and a block that several of
+// them keep is fetched once (the LoSA step: 20 rows per key head, 8 key heads,
+// one XCD each).
 #include "common.h"
 
 namespace basa {
@@ -43,7 +50,7 @@ struct RowArgs {
   void* o;
   float* lse;
   const int32_t* q_rows;
-  int64_t len_q, lists, rows_total;
+  int64_t len_q, lists, rows_total, chunk;
   int heads_q, heads_kv, group, block_k;
   float scale_log2;
 };
@@ -175,8 +182,9 @@ __global__ __launch_bounds__(NW * 64) void attn_row_kernel(RowArgs a) {
   __shared__ float part_m[NW], part_l[NW];
   __shared__ float part_o[NW][D];
 
-  const int64_t unit = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
-  if (unit >= a.rows_total) return;
+  const int64_t w = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+  const int64_t unit = (w % 8 + 8 * (w / 8 / a.chunk)) * a.chunk + (w / 8) % a.chunk;
+  if (unit >= a.rows_total) return;  // the last round of chunks is padded to all 8 XCDs
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = unit % a.lists;
@@ -315,8 +323,12 @@ hipError_t launch_attn_row(const basa_attn_desc* d, const void* q, int q_dtype, 
   a.scale_log2 = (float)(d->scale * 1.4426950408889634);
   a.rows_total = d->batch * d->heads_q * d->lists;
   if (a.rows_total == 0) return hipSuccess;
-  const int64_t gx = a.rows_total < 65536 ? a.rows_total : 65536;
-  const int64_t gy = (a.rows_total + gx - 1) / gx;
+  const int64_t per_kv = a.group * a.lists;  // consecutive rows of one key head
+  a.chunk = per_kv < 64 ? per_kv : 64;
+  const int64_t n_chunks = (a.rows_total + a.chunk - 1) / a.chunk;
+  const int64_t wgs = (n_chunks + 7) / 8 * 8 * a.chunk;  // chunk c on XCD c % 8
+  const int64_t gx = wgs < 65536 ? wgs : 65536;
+  const int64_t gy = (wgs + gx - 1) / gx;
   dim3 grid((unsigned)gx, (unsigned)gy);
   const int dd = (int)d->head_dim;
   const bool qb = q_dtype == BASA_BF16, ob = o_dtype == BASA_BF16;

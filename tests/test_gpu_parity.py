@@ -520,6 +520,35 @@ def test_attn_single_rows_long_lists(basa, block_k, d):
     assert max_err(lse[~empty], rl[~empty]) <= LSE_TOL
 
 
+@pytest.mark.parametrize("case", ["chunked_key_heads", "two_dim_grid"])
+def test_attn_single_rows_xcd_chunks(basa, case):
+    # The single-row kernel cuts the rows into chunks of up to 64 consecutive rows and
+    # runs chunk c on XCD c % 8: 150 rows per key head (chunks that end inside a key
+    # head, a padded last round) checked in full; 72,000 rows (a two-dimensional grid)
+    # checked on 256 sampled rows.
+    note(f"attn tile 1 XCD chunks: {case}")
+    g = np.random.Generator(np.random.PCG64(37))
+    if case == "chunked_key_heads":
+        b, hq, hkv, lq, d, nblk, count = 2, 6, 2, 50, 128, 64, 6
+    else:
+        b, hq, hkv, lq, d, nblk, count = 1, 2, 1, 36000, 64, 32, 2
+    q = wl.f32_to_bf16(g.standard_normal((b, hq, lq, d)).astype(np.float32))
+    k = wl.f32_to_bf16(g.standard_normal((b, hkv, nblk * 16, d)).astype(np.float32))
+    v = wl.f32_to_bf16(g.standard_normal((b, hkv, nblk * 16, d)).astype(np.float32))
+    idx = np.sort(g.random((b, hq, lq, nblk)).argsort(-1)[..., :count], axis=-1).astype(np.int32)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_attn(basa, q, [(idx, k, v, {})], 1, 16, scale, torch.float32)
+    if case == "chunked_key_heads":
+        ro, rl = orc.sparse_attention(q, k, v, idx, 1, 16, scale)
+        assert max_err(o, ro) <= 1e-4 and max_err(lse, rl) <= 1e-4
+    else:
+        rows = np.sort(g.choice(lq, 256, replace=False)).astype(np.int32)[None]
+        ro, rl = orc.sparse_attention(q, k, v, idx[:, :, rows[0]], 1, 16, scale, q_rows=rows)
+        assert max_err(o[:, :, rows[0]], ro[:, :, rows[0]]) <= 1e-4
+        assert max_err(lse[:, :, rows[0]], rl[:, :, rows[0]]) <= 1e-4
+        assert np.isfinite(lse).all()
+
+
 # --------------------------------------------------------------------------- merge
 
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.float32, torch.bfloat16), (torch.bfloat16, torch.float32),
