@@ -317,9 +317,10 @@ class LosaStep:
     The step's six calls are validated once, here; step() only issues them.
     union_walk: give the prefix attention its workspace, so that each key
     head's union of kept blocks is read once.  The default (False) lets every
-    row walk its own list: on the 64K-prefix workload that takes 29 us against
-    44 us for the union walk (both are bound by the latency of their block
-    chains; blocks that several rows keep are found in the cache).
+    row walk its own list: on the 64K-prefix workload that takes 27 us against
+    45 us for the union walk (the rows of a key head run on one XCD, whose L2
+    serves the blocks several of them keep; the union walk is bound by the
+    latency of its block chains and needs a second launch for its partials).
     """
 
     def __init__(self, q_cur, q_prev, k_prefix, v_prefix, k_block, v_block, cache_o, cache_lse,
