@@ -245,13 +245,19 @@ def sparsed_stage(torch, wl, basa) -> dict:
     w = wl.WORKLOADS["dlm16k"]
     x = wl.generate("dlm16k")
     f = SparsedForward(dev(x["q"]), dev(x["k"]), dev(x["v"]), w.block, w.tokens // 2, 0.3, w.scale)
-    t_mass = _time(torch, lambda: basa.basa_block_mass(f.q, f.k, w.block, f.mass, f.scale), reps=2)
+    t_mass = _time(torch, lambda: basa.basa_block_mass(f.q, f.k, w.block, f.mass, f.scale,
+                                                       workspace=f.mass_ws), reps=2)
+    t_mass2 = _time(torch, lambda: basa.basa_block_mass(f.q, f.k, w.block, f.mass, f.scale), reps=2)
     t_sel = _time(torch, lambda: basa.basa_select_ranges(f.mass, f.split, f.k_lo, f.k_hi, f.idx))
     f.pattern()
     t_attn = _time(torch, f.attend)
-    dense_fp64 = 2 * 2.0 * w.heads * w.tokens * w.tokens * w.head_dim  # two Q K^T passes
+    dense_fp64 = 2.0 * w.heads * w.tokens * w.tokens * w.head_dim  # one Q K^T product
     kept = f.k_lo + f.k_hi
     out = {"block_mass_ms": t_mass, "block_mass_fp64_TFLOP/s": dense_fp64 / (t_mass * 1e-3) / 1e12,
+           "block_mass_frac_fp64": dense_fp64 / (t_mass * 1e-3) / 1e12 / 78.6,
+           "block_mass_two_pass_ms": t_mass2,
+           "block_mass_note": "algorithmic flops: one float64 scale*Q*K^T product; the one-pass form "
+                              "(workspace) computes it once, the two-pass form twice",
            "select_ranges_ms": t_sel, "kept_blocks": kept, "attn_ms": t_attn,
            "attn_TFLOP/s": 4.0 * w.block ** 3 * w.heads * w.blocks * kept / (t_attn * 1e-3) / 1e12}
     del f

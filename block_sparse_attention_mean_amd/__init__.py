@@ -28,7 +28,7 @@ EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "ba
            "basa_select_static", "basa_pool_select", "basa_pool_select_workspace", "basa_attn",
            "basa_attn_workspace",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
-           "basa_block_mass", "basa_select_ranges", "basa_block_radius")
+           "basa_block_mass", "basa_block_mass_workspace", "basa_select_ranges", "basa_block_radius")
 
 
 class BasaError(RuntimeError):
@@ -105,7 +105,9 @@ def _load() -> ctypes.CDLL:
                                       ctypes.c_double, vp, vp]
     lib.basa_block_mass.restype = i32
     lib.basa_block_mass.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
-                                    vp, vp]
+                                    vp, vp, i64, vp]
+    lib.basa_block_mass_workspace.restype = i32
+    lib.basa_block_mass_workspace.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.basa_select_ranges.restype = i32
     lib.basa_select_ranges.argtypes = [vp, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.basa_block_radius.restype = i32
@@ -488,10 +490,22 @@ def basa_pool_moments(x: torch.Tensor, block: int, out: torch.Tensor, role: int,
                                                       float(scale), float(beta), _ptr(out), _stream()))
 
 
+def basa_block_mass_workspace(q: torch.Tensor, k: torch.Tensor, block: int) -> int:
+    """Bytes of workspace that let basa_block_mass run in one pass (0: this shape never does)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, len, head_dim]")
+    b, hq, lq, d = q.shape
+    out = ctypes.c_int64(0)
+    _check("basa_block_mass_workspace",
+           lib.basa_block_mass_workspace(b, hq, lq, k.shape[2], d, block, ctypes.byref(out)))
+    return out.value
+
+
 def basa_block_mass(q: torch.Tensor, k: torch.Tensor, block: int, mass: torch.Tensor,
-                    scale: float) -> None:
+                    scale: float, workspace: torch.Tensor | None = None) -> None:
     """mass [B, Hq, Lq/block, Lk/block] float64 <- the dense attention map's
-    block mass (rows sum to 1) for q [B, Hq, Lq, d], k [B, Hkv, Lk, d]."""
+    block mass (rows sum to 1) for q [B, Hq, Lq, d], k [B, Hkv, Lk, d].
+    workspace: optional uint8 device scratch (see basa_block_mass_workspace)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [batch, heads, len, head_dim]")
     b, hq, lq, d = q.shape
@@ -501,9 +515,12 @@ def basa_block_mass(q: torch.Tensor, k: torch.Tensor, block: int, mass: torch.Te
         raise TypeError("mass is float64")
     if block > 0 and lq % block == 0 and k.shape[2] % block == 0:
         _shape("mass", mass, (b, hq, lq // block, k.shape[2] // block))
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    ws, n_ws = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     _check("basa_block_mass", lib.basa_block_mass(_ptr(q), _ptr(k), _dt(q), b, hq, k.shape[1], lq,
                                                   k.shape[2], d, block, float(scale), _ptr(mass),
-                                                  _stream()))
+                                                  ws, n_ws, _stream()))
 
 
 def basa_select_ranges(scores: torch.Tensor, split: int, k_lo: int, k_hi: int,
@@ -586,5 +603,5 @@ __all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_sta
            "basa_attn_workspace", "prepare_attn", "prepare_pool", "prepare_select", "prepare_merge", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",
            "SELECT_CHANGE", "basa_rank_workspace", "basa_rank", "basa_permute", "PERMUTE_GATHER",
-           "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass",
+           "PERMUTE_SCATTER", "basa_pool_moments", "MOMENTS_QUERY", "MOMENTS_KEY", "basa_block_mass", "basa_block_mass_workspace",
            "basa_select_ranges", "basa_block_radius"]

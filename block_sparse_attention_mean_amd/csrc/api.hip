@@ -256,7 +256,8 @@ int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse
 
 int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
                     int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim, int64_t block,
-                    double scale, double* mass, void* stream) {
+                    double scale, double* mass, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
   try {
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv != 0) return BASA_E_SHAPE;
     if (head_dim < 8 || head_dim > 128 || head_dim % 8 != 0) return BASA_E_SHAPE;
@@ -267,9 +268,22 @@ int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int6
     if (batch == 0 || len_q == 0 || len_k == 0) return BASA_OK;
     if (!q || !k || !mass) return BASA_E_NULLPTR;
     if (!aligned16(q) || !aligned16(k) || !aligned16(mass)) return BASA_E_ALIGN;
+    const int64_t need = basa::block_mass_workspace_bytes(batch, heads_q, len_q, len_k, head_dim, block);
+    void* ws = need > 0 && workspace && aligned16(workspace) && workspace_bytes >= need ? workspace : nullptr;
     return from_hip(basa::launch_block_mass(q, k, dtype, batch, heads_q, heads_kv, len_q, len_k,
-                                            head_dim, block, scale, mass,
+                                            head_dim, block, scale, mass, ws,
                                             static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
+int basa_block_mass_workspace(int64_t batch, int64_t heads_q, int64_t len_q, int64_t len_k,
+                              int64_t head_dim, int64_t block, int64_t* bytes) {
+  try {
+    if (!bytes) return BASA_E_NULLPTR;
+    *bytes = basa::block_mass_workspace_bytes(batch, heads_q, len_q, len_k, head_dim, block);
+    return BASA_OK;
   } catch (...) {
     return BASA_E_LAUNCH;
   }

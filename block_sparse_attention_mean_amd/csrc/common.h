@@ -111,9 +111,12 @@ hipError_t launch_merge(int64_t rows, int64_t head_dim, const void* o_a, const f
 hipError_t launch_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                           int64_t block, int role, double scale, double beta, double* out,
                           hipStream_t s);
+// workspace: block_mass_workspace_bytes() of device scratch (the one-pass kernel), or null
+int64_t block_mass_workspace_bytes(int64_t batch, int64_t heads_q, int64_t len_q, int64_t len_k,
+                                   int64_t head_dim, int64_t block);
 hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
                              int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim,
-                             int64_t block, double scale, double* mass, hipStream_t s);
+                             int64_t block, double scale, double* mass, void* workspace, hipStream_t s);
 hipError_t launch_select_ranges(const double* scores, int64_t rows, int64_t n, int64_t split,
                                 int k_lo, int k_hi, int32_t* idx, hipStream_t s);
 hipError_t launch_radius(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,

@@ -317,11 +317,141 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// One pass over the keys (with a workspace).  The two passes above compute
+// every logit twice: once for the row LSE, once for exp(s - LSE).  Here, for
+// each (row, key block), the walk keeps the block's own running max and sum of
+// exp(s - max) (online inside the block, so nothing overflows), and when the
+// block closes the 16 lanes of the row combine theirs and write (max, sum) to
+// the workspace.  After the walk each row's LSE is formed from its (max, sum)
+// pairs, and mass[gq][gk] = (1/block) sum_i sum_gk,i exp(max_gk,i - LSE_i).
+// The same sums, one exponential per logit instead of two; the result differs
+// from the two-pass kernel only in float64 rounding order.
+// ---------------------------------------------------------------------------
+template <typename T, int KC>
+__global__ __launch_bounds__(MASS_NT, 2) void block_mass_onepass_kernel(MassArgs a, double2* ws) {
+  __shared__ double kc0[KC * (MASS_MAX_D + 2)];
+  __shared__ double kc1[KC * (MASS_MAX_D + 2)];
+  __shared__ double s_lse[16 * 4 * MM_TILES];
+  const int64_t nq = a.len_q / a.block, nk = a.len_k / a.block;
+  const int64_t gq = blockIdx.x % nq;
+  const int64_t bh = blockIdx.x / nq;
+  const int h = (int)(bh % a.heads_q);
+  const int64_t b = bh / a.heads_q;
+  const int hk = h / (a.heads_q / a.heads_kv);
+  const int d = a.d, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = a.block / 16;
+  const T* qh = static_cast<const T*>(a.q) + ((b * a.heads_q + h) * a.len_q + gq * a.block) * d;
+  const T* kh = static_cast<const T*>(a.k) + (b * a.heads_kv + hk) * a.len_k * d;
+  double2* wsb = ws + (bh * nq + gq) * nk * a.block;  // [key block][row]: (max, sum)
+  double aq[MM_TILES][MM_STEPS];
+#pragma unroll
+  for (int t = 0; t < MM_TILES; ++t) {
+    const int tile = wave + 4 * t;
+#pragma unroll
+    for (int s = 0; s < MM_STEPS; ++s)
+      aq[t][s] = (tile < n_tiles && 4 * s < d)
+                     ? (double)to_f32<T>(qh[(int64_t)(tile * 16 + (lane & 15)) * d + 4 * s + (lane >> 4)])
+                     : 0.0;
+  }
+  // block-local online state of this lane's keys (rows lane/16 + 4r of each tile)
+  double mb[MM_TILES][4], bb[MM_TILES][4];
+#pragma unroll
+  for (int t = 0; t < MM_TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mb[t][r] = -INFINITY;
+      bb[t][r] = 0.0;
+    }
+  const int64_t n_chunks = a.len_k / KC;
+  const int64_t cpb = a.block / KC;  // chunks per key block
+  KeyStage<T, KC> st;
+  st.load(kh, d, 0);
+  st.store(kc0, d);
+  __syncthreads();
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const double* kc = (c & 1) ? kc1 : kc0;
+    if (c + 1 < n_chunks) st.load(kh, d, (c + 1) * KC);
+#pragma unroll
+    for (int t = 0; t < MM_TILES; ++t) {
+      if (wave + 4 * t >= n_tiles) continue;  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < KC / 16; ++u) {
+        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double v = a.scale * sv[r];
+          if (v > mb[t][r]) {
+            bb[t][r] = bb[t][r] * exp(mb[t][r] - v) + 1.0;
+            mb[t][r] = v;
+          } else {
+            bb[t][r] += exp(v - mb[t][r]);
+          }
+        }
+      }
+    }
+    if ((c + 1) % cpb == 0) {  // key block gk closes: each row's (max, sum) to the workspace
+      const int64_t gk = c / cpb;
+#pragma unroll
+      for (int t = 0; t < MM_TILES; ++t) {
+        if (wave + 4 * t >= n_tiles) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          double mx = mb[t][r];
+          for (int off = 1; off < 16; off <<= 1) mx = fmax(mx, __shfl_xor(mx, off));
+          double sm = mb[t][r] == -INFINITY ? 0.0 : bb[t][r] * exp(mb[t][r] - mx);
+          for (int off = 1; off < 16; off <<= 1) sm += __shfl_xor(sm, off);
+          if ((lane & 15) == 0)
+            wsb[gk * a.block + (wave + 4 * t) * 16 + (lane >> 4) + 4 * r] = double2{mx, sm};
+          mb[t][r] = -INFINITY;
+          bb[t][r] = 0.0;
+        }
+      }
+    }
+    if (c + 1 < n_chunks) st.store((c & 1) ? kc0 : kc1, d);
+    __syncthreads();
+  }
+  // the workspace writes of every wave are visible to the workgroup after this barrier
+  __syncthreads();
+  // LSE of each row from its per-block (max, sum)
+  for (int i = threadIdx.x; i < a.block; i += MASS_NT) {
+    double mx = -INFINITY;
+    for (int64_t gk = 0; gk < nk; ++gk) mx = fmax(mx, wsb[gk * a.block + i].x);
+    double sm = 0.0;
+    for (int64_t gk = 0; gk < nk; ++gk) {
+      const double2 e = wsb[gk * a.block + i];
+      if (e.x != -INFINITY) sm += e.y * exp(e.x - mx);
+    }
+    s_lse[i] = mx + log(sm);
+  }
+  __syncthreads();
+  // mass of each key block: its rows' sums rescaled to their LSE, in row order
+  double* out = a.mass + (bh * nq + gq) * nk;
+  for (int64_t gk = threadIdx.x; gk < nk; gk += MASS_NT) {
+    double sum = 0.0;
+    for (int i = 0; i < a.block; ++i) {
+      const double2 e = wsb[gk * a.block + i];
+      if (e.x != -INFINITY) sum += e.y * exp(e.x - s_lse[i]);
+    }
+    out[gk] = sum / a.block;
+  }
+}
+
 }  // namespace
+
+int64_t block_mass_workspace_bytes(int64_t batch, int64_t heads_q, int64_t len_q, int64_t len_k,
+                                   int64_t head_dim, int64_t block) {
+  // the one-pass kernel serves the float64 matrix-core shapes
+  if (batch < 1 || heads_q < 1 || block < 16 || block % 16 != 0 || block > 16 * 4 * MM_TILES ||
+      head_dim % 4 != 0 || head_dim > MASS_MAX_D || len_q < block || len_k < block)
+    return 0;
+  return batch * heads_q * len_q * (len_k / block) * (int64_t)sizeof(double2);
+}
 
 hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
                              int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim,
-                             int64_t block, double scale, double* mass, hipStream_t s) {
+                             int64_t block, double scale, double* mass, void* workspace, hipStream_t s) {
   MassArgs a;
   a.q = q;
   a.k = k;
@@ -335,7 +465,20 @@ hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t ba
   a.scale = scale;
   const dim3 grid((unsigned)(batch * heads_q * (len_q / block)));
   const bool mfma = block % 16 == 0 && block <= 16 * 4 * MM_TILES && head_dim % 4 == 0;
-  if (mfma && block % 32 == 0) {
+  if (mfma && workspace) {  // the caller checked its size against block_mass_workspace_bytes
+    double2* ws = static_cast<double2*>(workspace);
+    if (block % 32 == 0) {
+      if (dtype == BASA_BF16)
+        block_mass_onepass_kernel<uint16_t, 32><<<grid, MASS_NT, 0, s>>>(a, ws);
+      else
+        block_mass_onepass_kernel<float, 32><<<grid, MASS_NT, 0, s>>>(a, ws);
+    } else {
+      if (dtype == BASA_BF16)
+        block_mass_onepass_kernel<uint16_t, 16><<<grid, MASS_NT, 0, s>>>(a, ws);
+      else
+        block_mass_onepass_kernel<float, 16><<<grid, MASS_NT, 0, s>>>(a, ws);
+    }
+  } else if (mfma && block % 32 == 0) {
     if (dtype == BASA_BF16)
       block_mass_mfma_kernel<uint16_t, 32><<<grid, MASS_NT, 0, s>>>(a);
     else

@@ -27,7 +27,8 @@ import math
 import torch
 
 from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS,
-               SELECT_CHANGE, basa_attn, basa_attn_workspace, basa_block_mass, basa_merge,
+               SELECT_CHANGE, basa_attn, basa_attn_workspace, basa_block_mass,
+               basa_block_mass_workspace, basa_merge,
                basa_permute, basa_pool, basa_pool_moments, basa_rank, basa_rank_workspace,
                basa_select, basa_select_ranges, basa_select_workspace, kv_segment, prepare_attn,
                prepare_merge, prepare_pool, prepare_select)
@@ -196,9 +197,12 @@ class SparsedForward:
         self.o = torch.empty(q.shape, dtype=o_dtype or q.dtype, device=q.device)
         self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
         self.attn_ws = None  # tile-order workspace of the attention, sized at the first attend()
+        # the block mass in one pass over the keys: one (max, sum) pair per (query row, key block)
+        n_mws = basa_block_mass_workspace(q, k, block)
+        self.mass_ws = _empty(n_mws, dtype=torch.uint8, like=q) if n_mws > 0 else None
 
     def pattern(self):
-        basa_block_mass(self.q, self.k, self.block, self.mass, self.scale)
+        basa_block_mass(self.q, self.k, self.block, self.mass, self.scale, workspace=self.mass_ws)
         basa_select_ranges(self.mass, self.split, self.k_lo, self.k_hi, self.idx)
 
     def attend(self, q=None, k=None, v=None):

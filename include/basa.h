@@ -384,7 +384,15 @@ int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse
  *   k     device [batch][heads_kv][len_k][head_dim] of dtype; query head h
  *         reads key head h / (heads_q / heads_kv)
  *   mass  device float64 [batch][heads_q][len_q/block][len_k/block]
- * A dense pass: it costs two scale*Q*K^T products in float64.
+ *   workspace  optional device scratch owned by the caller (NULL: none), 16-byte
+ *         aligned, of workspace_bytes.  With at least basa_block_mass_workspace()
+ *         bytes the mass is formed in one pass over the keys: per (row, key
+ *         block) the block's own max and sum of exp(s - max) go to the
+ *         workspace, the row LSE follows from them, and the mass from both
+ *         (one float64 scale*Q*K^T product).  Without it, two passes (the row
+ *         LSE first, then the sums of exp(s - LSE)).  The two differ only in
+ *         float64 rounding order.  The call overwrites the workspace; calls
+ *         that overlap in time must not share it.
  * Errors: BASA_E_SHAPE for non-positive heads, heads_q not a multiple of
  * heads_kv, head_dim not a multiple of 8 or above 128, block not a power of
  * two in [4, 256], lengths not multiples of block, or a scale that is not
@@ -392,7 +400,18 @@ int basa_merge(int64_t rows, int64_t head_dim, const void* o_a, const float* lse
  */
 int basa_block_mass(const void* q, const void* k, int dtype, int64_t batch, int64_t heads_q,
                     int64_t heads_kv, int64_t len_q, int64_t len_k, int64_t head_dim, int64_t block,
-                    double scale, double* mass, void* stream);
+                    double scale, double* mass, void* workspace, int64_t workspace_bytes,
+                    void* stream);
+
+/*
+ * basa_block_mass_workspace - bytes of workspace that let basa_block_mass take
+ * its one-pass form (0: this shape never does: blocks of 16..128 rows that are
+ * multiples of 16, head_dim a multiple of 4 and at most 128):
+ * batch * heads_q * len_q * (len_k / block) * 16 bytes.
+ * Errors: BASA_E_NULLPTR for a NULL bytes.
+ */
+int basa_block_mass_workspace(int64_t batch, int64_t heads_q, int64_t len_q, int64_t len_k,
+                              int64_t head_dim, int64_t block, int64_t* bytes);
 
 /*
  * basa_select_ranges - per row, the best columns of two column ranges.

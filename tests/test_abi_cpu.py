@@ -299,8 +299,15 @@ def test_pool_moments_validation():
 
 
 def mass(q=FAKE, k=FAKE, dt=basa.BF16, b=1, hq=4, hkv=2, lq=256, lk=256, d=64, block=32, scale=0.1,
-         out=FAKE):
-    return basa.lib.basa_block_mass(q, k, dt, b, hq, hkv, lq, lk, d, block, scale, out, None)
+         out=FAKE, ws=None, ws_bytes=0):
+    return basa.lib.basa_block_mass(q, k, dt, b, hq, hkv, lq, lk, d, block, scale, out, ws, ws_bytes,
+                                    None)
+
+
+def mass_ws(b=1, hq=4, lq=256, lk=256, d=64, block=32):
+    out = ctypes.c_int64(-1)
+    assert basa.lib.basa_block_mass_workspace(b, hq, lq, lk, d, block, ctypes.byref(out)) == OK
+    return out.value
 
 
 def test_block_mass_validation():
@@ -314,6 +321,20 @@ def test_block_mass_validation():
     assert mass(k=None) == NULLPTR
     assert mass(out=MISALIGNED) == ALIGN
     assert mass(b=0, q=None, k=None, out=None) == OK
+    assert mass(k=None, ws=FAKE, ws_bytes=1 << 20) == NULLPTR   # the workspace checks nothing else
+    assert mass(out=MISALIGNED, ws=FAKE, ws_bytes=1 << 20) == ALIGN
+
+
+def test_block_mass_workspace_sizes():
+    # one (max, sum) pair of float64 per (query row, key block) on the matrix-core shapes
+    assert mass_ws() == 1 * 4 * 256 * (256 // 32) * 16
+    assert mass_ws(b=2, hq=8, lq=16384, lk=16384, d=128, block=128) == 2 * 8 * 16384 * 128 * 16
+    assert mass_ws(block=16) == 4 * 256 * 16 * 16
+    assert mass_ws(block=8) == 0          # not a multiple of 16: the one-thread-per-row kernel
+    assert mass_ws(block=256) == 0        # above the matrix-core kernel's 128 rows
+    assert mass_ws(d=132) == 0
+    assert mass_ws(b=0) == 0
+    assert basa.lib.basa_block_mass_workspace(1, 4, 256, 256, 64, 32, None) == NULLPTR
 
 
 def ranges(s=FAKE, rows=4, n=128, split=64, lo=20, hi=20, idx=FAKE):

@@ -25,11 +25,18 @@ def basa():
     return mod
 
 
-def gpu_mass(basa, q, k, block, scale):
+def gpu_mass(basa, q, k, block, scale, one_pass=False):
+    """one_pass: give the call the workspace basa_block_mass_workspace asks for
+    (filled with 0x5A, not zeroed); shapes outside the one-pass kernel get none."""
     qt, kt = dev(q), dev(k)
     b, h, lq, _ = qt.shape
     m = torch.empty(b, h, lq // block, kt.shape[2] // block, dtype=torch.float64, device="cuda")
-    basa.basa_block_mass(qt, kt, block, m, scale)
+    ws = None
+    if one_pass:
+        n = basa.basa_block_mass_workspace(qt, kt, block)
+        if n > 0:
+            ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    basa.basa_block_mass(qt, kt, block, m, scale, workspace=ws)
     torch.cuda.synchronize()
     return host(m)
 
@@ -38,22 +45,44 @@ def rel_err(a, b):
     return float(np.abs(a - b).max() / np.abs(b).max())
 
 
+@pytest.mark.parametrize("one_pass", [False, True])
 @pytest.mark.parametrize("kind,hq,hkv,length,d,block", [
     ("f32", 2, 2, 1024, 64, 64), ("bf16", 3, 3, 2048, 128, 128), ("bf16", 4, 2, 1024, 64, 32),
     ("bf16", 1, 1, 512, 128, 16), ("f32", 1, 1, 256, 8, 4), ("f32", 2, 1, 512, 64, 16),
     ("bf16", 2, 2, 256, 24, 32), ("f32", 1, 1, 128, 8, 16)])
-def test_block_mass_matches_oracle(basa, kind, hq, hkv, length, d, block):
-    note(f"block mass {kind} H{hq}/{hkv} L{length} d{d} block{block}")
+def test_block_mass_matches_oracle(basa, kind, hq, hkv, length, d, block, one_pass):
+    note(f"block mass {kind} H{hq}/{hkv} L{length} d{d} block{block} one pass {one_pass}")
     g = np.random.Generator(np.random.PCG64(length + d + block))
     q = g.standard_normal((1, hq, length, d)) * g.uniform(0.5, 2.0, (1, hq, length, 1))
     k = g.standard_normal((1, hkv, length, d))
     conv = (lambda a: wl.f32_to_bf16(a.astype(np.float32))) if kind == "bf16" else (lambda a: a.astype(np.float32))
     q, k = conv(q), conv(k)
     scale = 1.0 / np.sqrt(d)
-    got = gpu_mass(basa, q, k, block, scale)
+    got = gpu_mass(basa, q, k, block, scale, one_pass)
     ref = orc.block_mass(q, k, block, scale)
     assert rel_err(got, ref) < 1e-12
     assert np.abs(got.sum(axis=-1) - 1.0).max() < 1e-12
+
+
+@pytest.mark.parametrize("block", [128, 16])
+def test_block_mass_one_pass_large_logits_and_two_pass(basa, block):
+    # rows scaled so that logits reach several hundred (each key block's own max
+    # keeps the sums finite), keys with one planted block per head: the one-pass
+    # form against the oracle and against the two-pass form
+    note(f"block mass one pass, large logits, block {block}")
+    g = np.random.Generator(np.random.PCG64(77 + block))
+    d, length = 128, 2048
+    q = g.standard_normal((1, 2, length, d)) * g.uniform(1.0, 60.0, (1, 2, length, 1))
+    k = g.standard_normal((1, 2, length, d))
+    k[0, :, 5 * block:6 * block] += 3.0 * q[0, :, :block].mean(axis=1, keepdims=True) / 60.0
+    q, k = wl.f32_to_bf16(q.astype(np.float32)), wl.f32_to_bf16(k.astype(np.float32))
+    scale = 1.0 / np.sqrt(d)
+    one = gpu_mass(basa, q, k, block, scale, one_pass=True)
+    two = gpu_mass(basa, q, k, block, scale, one_pass=False)
+    ref = orc.block_mass(q, k, block, scale)
+    assert np.isfinite(one).all()
+    assert rel_err(one, ref) < 1e-12 and rel_err(one, two) < 1e-12
+    assert np.abs(one.sum(axis=-1) - 1.0).max() < 1e-12
 
 
 @pytest.mark.parametrize("n,split,k_lo,k_hi", [(37, 10, 3, 5), (128, 64, 20, 20), (512, 0, 0, 100),
