@@ -16,6 +16,8 @@
 // below; other blocks take this one-thread-per-row kernel.
 #include "common.h"
 
+#include <type_traits>
+
 namespace basa {
 namespace {
 
@@ -188,19 +190,36 @@ struct KeyStage {
   }
 };
 
-// the 16x16 logits of tile t against the 16 keys of sub-tile u of the staged chunk
-__device__ __forceinline__ f64x4 tile_logits(const double (*aq)[MM_STEPS], int t, const double* kc,
-                                             int u, int d, int lane) {
-  const int str = d + 2;
-  const double* kb = kc + (u * 16 + (lane & 15)) * str + (lane >> 4);
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+// The 16x16 logits of tile t against every 16-key sub-tile of the staged chunk:
+// the KC/16 accumulation chains advance together, so the matrix core always has
+// an independent product to start.  NS > 0: head_dim = 4*NS is a compile-time
+// constant, so every key read has a fixed offset and none waits behind a branch;
+// NS = 0: any head_dim that is a multiple of 4 (steps past it are skipped).
+template <int KC, int NS>
+__device__ __forceinline__ void chunk_logits(const double (*aq)[MM_STEPS], int t, const double* kc,
+                                             int d, int lane, f64x4 (&sv)[KC / 16]) {
+  constexpr int NU = KC / 16;
+  const int str = NS > 0 ? 4 * NS + 2 : d + 2;
+  const double* kb = kc + (lane & 15) * str + (lane >> 4);
 #pragma unroll
-  for (int s = 0; s < MM_STEPS; ++s)
-    if (4 * s < d) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aq[t][s], kb[4 * s], acc, 0, 0, 0);
-  return acc;
+  for (int u = 0; u < NU; ++u) sv[u] = f64x4{0.0, 0.0, 0.0, 0.0};
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        sv[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(aq[t][s], kb[u * 16 * str + 4 * s], sv[u], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int s = 0; s < MM_STEPS; ++s)
+      if (4 * s < d)
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          sv[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(aq[t][s], kb[u * 16 * str + 4 * s], sv[u], 0, 0, 0);
+  }
 }
 
-template <typename T, int KC>
+template <typename T, int KC, int NS>
 __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a) {
   __shared__ double kc0[KC * (MASS_MAX_D + 2)];
   __shared__ double kc1[KC * (MASS_MAX_D + 2)];
@@ -247,12 +266,13 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a)
 #pragma unroll
     for (int t = 0; t < MM_TILES; ++t) {
       if (wave + 4 * t >= n_tiles) continue;  // wave-uniform
+      f64x4 sv[KC / 16];
+      chunk_logits<KC, NS>(aq, t, kc, d, lane, sv);
 #pragma unroll
       for (int u = 0; u < KC / 16; ++u) {
-        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const double v = a.scale * sv[r];
+          const double v = a.scale * sv[u][r];
           if (v > m[t][r]) {
             l[t][r] = l[t][r] * exp(m[t][r] - v) + 1.0;
             m[t][r] = v;
@@ -295,11 +315,12 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a)
 #pragma unroll
     for (int t = 0; t < MM_TILES; ++t) {
       if (wave + 4 * t >= n_tiles) continue;
+      f64x4 sv[KC / 16];
+      chunk_logits<KC, NS>(aq, t, kc, d, lane, sv);
 #pragma unroll
       for (int u = 0; u < KC / 16; ++u) {
-        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += exp(a.scale * sv[r] - lse[t][r]);
+        for (int r = 0; r < 4; ++r) part += exp(a.scale * sv[u][r] - lse[t][r]);
       }
     }
     const bool closes = (c + 1) % cpb == 0;
@@ -328,7 +349,7 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a)
 // The same sums, one exponential per logit instead of two; the result differs
 // from the two-pass kernel only in float64 rounding order.
 // ---------------------------------------------------------------------------
-template <typename T, int KC>
+template <typename T, int KC, int NS>
 __global__ __launch_bounds__(MASS_NT, 2) void block_mass_onepass_kernel(MassArgs a, double2* ws) {
   __shared__ double kc0[KC * (MASS_MAX_D + 2)];
   __shared__ double kc1[KC * (MASS_MAX_D + 2)];
@@ -376,12 +397,13 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_onepass_kernel(MassArgs
 #pragma unroll
     for (int t = 0; t < MM_TILES; ++t) {
       if (wave + 4 * t >= n_tiles) continue;  // wave-uniform
+      f64x4 sv[KC / 16];
+      chunk_logits<KC, NS>(aq, t, kc, d, lane, sv);
 #pragma unroll
       for (int u = 0; u < KC / 16; ++u) {
-        const f64x4 sv = tile_logits(aq, t, kc, u, d, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const double v = a.scale * sv[r];
+          const double v = a.scale * sv[u][r];
           if (v > mb[t][r]) {
             bb[t][r] = bb[t][r] * exp(mb[t][r] - v) + 1.0;
             mb[t][r] = v;
@@ -438,6 +460,8 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_onepass_kernel(MassArgs
   }
 }
 
+template <typename T> struct TypeTag { using type = T; };
+
 }  // namespace
 
 int64_t block_mass_workspace_bytes(int64_t batch, int64_t heads_q, int64_t len_q, int64_t len_k,
@@ -465,29 +489,36 @@ hipError_t launch_block_mass(const void* q, const void* k, int dtype, int64_t ba
   a.scale = scale;
   const dim3 grid((unsigned)(batch * heads_q * (len_q / block)));
   const bool mfma = block % 16 == 0 && block <= 16 * 4 * MM_TILES && head_dim % 4 == 0;
-  if (mfma && workspace) {  // the caller checked its size against block_mass_workspace_bytes
-    double2* ws = static_cast<double2*>(workspace);
-    if (block % 32 == 0) {
-      if (dtype == BASA_BF16)
-        block_mass_onepass_kernel<uint16_t, 32><<<grid, MASS_NT, 0, s>>>(a, ws);
+  if (mfma) {
+    // head_dim 64 or 128 at compile time; other multiples of 4 through the general steps
+    const int ns = head_dim == 128 ? 32 : head_dim == 64 ? 16 : 0;
+    double2* ws = static_cast<double2*>(workspace);  // the caller checked its size
+    auto go = [&](auto tt, auto kc, auto nsc) {
+      using T = typename decltype(tt)::type;
+      constexpr int KC = decltype(kc)::value, NS = decltype(nsc)::value;
+      if (ws)
+        block_mass_onepass_kernel<T, KC, NS><<<grid, MASS_NT, 0, s>>>(a, ws);
       else
-        block_mass_onepass_kernel<float, 32><<<grid, MASS_NT, 0, s>>>(a, ws);
-    } else {
-      if (dtype == BASA_BF16)
-        block_mass_onepass_kernel<uint16_t, 16><<<grid, MASS_NT, 0, s>>>(a, ws);
+        block_mass_mfma_kernel<T, KC, NS><<<grid, MASS_NT, 0, s>>>(a);
+    };
+    auto by_ns = [&](auto tt, auto kc) {
+      if (ns == 32)
+        go(tt, kc, std::integral_constant<int, 32>());
+      else if (ns == 16)
+        go(tt, kc, std::integral_constant<int, 16>());
       else
-        block_mass_onepass_kernel<float, 16><<<grid, MASS_NT, 0, s>>>(a, ws);
-    }
-  } else if (mfma && block % 32 == 0) {
+        go(tt, kc, std::integral_constant<int, 0>());
+    };
+    auto by_kc = [&](auto tt) {
+      if (block % 32 == 0)
+        by_ns(tt, std::integral_constant<int, 32>());
+      else
+        by_ns(tt, std::integral_constant<int, 16>());
+    };
     if (dtype == BASA_BF16)
-      block_mass_mfma_kernel<uint16_t, 32><<<grid, MASS_NT, 0, s>>>(a);
+      by_kc(TypeTag<uint16_t>());
     else
-      block_mass_mfma_kernel<float, 32><<<grid, MASS_NT, 0, s>>>(a);
-  } else if (mfma) {
-    if (dtype == BASA_BF16)
-      block_mass_mfma_kernel<uint16_t, 16><<<grid, MASS_NT, 0, s>>>(a);
-    else
-      block_mass_mfma_kernel<float, 16><<<grid, MASS_NT, 0, s>>>(a);
+      by_kc(TypeTag<float>());
   } else if (dtype == BASA_BF16) {
     block_mass_kernel<uint16_t><<<grid, MASS_NT, 0, s>>>(a);
   } else {
