@@ -190,6 +190,19 @@ struct KeyStage {
   }
 };
 
+// Online (max, sum of exp(s - max)) update with one exponential and no branch:
+// with d = v - m, a new maximum (d > 0) rescales the sum by exp(-d) and adds 1,
+// otherwise exp(d) is added; both are exp(-|d|), so lanes that disagree do not
+// make the wave evaluate the (software, float64) exponential twice.  The same
+// exponentials as the two-branch form; the sums can round differently only in
+// how the compiler fuses the multiply-add.
+__device__ __forceinline__ void online_add(double v, double& m, double& l) {
+  const double d = v - m;  // m = -inf at the start: d = +inf, e = 0, l = 0 * 0 + 1
+  const double e = exp(-fabs(d));
+  l = d > 0.0 ? l * e + 1.0 : l + e;
+  m = d > 0.0 ? v : m;
+}
+
 // The 16x16 logits of tile t against every 16-key sub-tile of the staged chunk:
 // the KC/16 accumulation chains advance together, so the matrix core always has
 // an independent product to start.  NS > 0: head_dim = 4*NS is a compile-time
@@ -273,12 +286,7 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_mfma_kernel(MassArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const double v = a.scale * sv[u][r];
-          if (v > m[t][r]) {
-            l[t][r] = l[t][r] * exp(m[t][r] - v) + 1.0;
-            m[t][r] = v;
-          } else {
-            l[t][r] += exp(v - m[t][r]);
-          }
+          online_add(v, m[t][r], l[t][r]);
         }
       }
     }
@@ -404,12 +412,7 @@ __global__ __launch_bounds__(MASS_NT, 2) void block_mass_onepass_kernel(MassArgs
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const double v = a.scale * sv[u][r];
-          if (v > mb[t][r]) {
-            bb[t][r] = bb[t][r] * exp(mb[t][r] - v) + 1.0;
-            mb[t][r] = v;
-          } else {
-            bb[t][r] += exp(v - mb[t][r]);
-          }
+          online_add(v, mb[t][r], bb[t][r]);
         }
       }
     }
