@@ -36,6 +36,7 @@ struct SelArgs {
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 typedef uint32_t u32x4_sel __attribute__((ext_vector_type(4)));
+typedef double f64x4_sel __attribute__((ext_vector_type(4)));
 
 // A wave-uniform element of read-only input through the constant address space,
 // so it is fetched with a scalar load.  (A vector load would share the in-order
@@ -50,6 +51,71 @@ __device__ __forceinline__ uint64_t readfirstlane64(uint64_t x) {
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
   const uint32_t h = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
   return ((uint64_t)h << 32) | l;
+}
+
+// Largest / smallest 32-bit value over the wave (every lane active): DPP
+// exchanges inside each row of 16 lanes (pairs, quad halves, half-row mirror,
+// row mirror), then the four rows' results read into scalars.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return pick(pick(r0, r1), pick(r2, r3));
+}
+
+// Largest and smallest valid key of the wave (at least one valid key), as
+// wave-uniform values: the high halves first, then the low halves among the
+// lanes whose high half is the extreme one.
+template <int KPL>
+__device__ __forceinline__ void wave_key_range(const uint64_t* key, const bool* valid,
+                                               uint64_t& hi, uint64_t& lo) {
+  uint64_t lmax = 0, lmin = ~0ull;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    if (valid[j]) {
+      lmax = key[j] > lmax ? key[j] : lmax;
+      lmin = key[j] < lmin ? key[j] : lmin;
+    }
+  const uint32_t hh = wave_ext_u32<true>((uint32_t)(lmax >> 32));
+  const uint32_t hl = wave_ext_u32<true>((uint32_t)(lmax >> 32) == hh ? (uint32_t)lmax : 0u);
+  const uint32_t lh = wave_ext_u32<false>((uint32_t)(lmin >> 32));
+  const uint32_t ll = wave_ext_u32<false>((uint32_t)(lmin >> 32) == lh ? (uint32_t)lmin : ~0u);
+  hi = ((uint64_t)hh << 32) | hl;
+  lo = ((uint64_t)lh << 32) | ll;
+}
+
+// Marks the keys of a wave-level top-k once its threshold T (the k-th largest
+// key) is known: every valid key above T, then the keys equal to T in candidate
+// order until k are taken.  With exact set, exactly k keys are at or above T and
+// those are taken.
+template <int KPL>
+__device__ __forceinline__ void select_at(const uint64_t* key, const bool* valid, int k,
+                                          uint64_t below, uint64_t thr, bool exact, bool* sel) {
+  if (exact) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sel[j] = valid[j] && key[j] >= thr;
+    return;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gt += popc64(__ballot(valid[j] && key[j] > thr));
+  const int need_eq = k - gt;
+  int eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool eq = valid[j] && key[j] == thr;
+    const uint64_t em = __ballot(eq);
+    const int eq_rank = eq_seen + popc64(em & below);
+    eq_seen += popc64(em);
+    sel[j] = (valid[j] && key[j] > thr) || (eq && eq_rank < need_eq);
+  }
 }
 
 // Wave-level top-k over KPL keys per lane in candidate order (lane + 64 j).
@@ -70,21 +136,8 @@ __device__ __forceinline__ void wave_topk(const uint64_t* key, const bool* valid
   }
   // Every valid key lies in [lo, hi], so all share the bits above the highest
   // bit where lo and hi differ: T has those bits, and the search starts below.
-  uint64_t hi = 0, lo = ~0ull;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j)
-    if (valid[j]) {
-      hi = key[j] > hi ? key[j] : hi;
-      lo = key[j] < lo ? key[j] : lo;
-    }
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) {
-    const uint64_t ho = __shfl_xor(hi, sh), lw = __shfl_xor(lo, sh);
-    hi = ho > hi ? ho : hi;
-    lo = lw < lo ? lw : lo;
-  }
-  hi = readfirstlane64(hi);  // every lane holds the same value after the butterfly
-  lo = readfirstlane64(lo);
+  uint64_t hi, lo;
+  wave_key_range<KPL>(key, valid, hi, lo);
   // diff == 0: all valid keys are equal, T = hi and the tie rule below takes the first k
   const uint64_t diff = hi ^ lo;
   const int top = diff ? 63 - __clzll(diff) : -1;
@@ -100,24 +153,7 @@ __device__ __forceinline__ void wave_topk(const uint64_t* key, const bool* valid
       if (cnt == k) { exact = true; break; }
     }
   }
-  if (exact) {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) sel[j] = valid[j] && key[j] >= thr;
-    return;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) gt += popc64(__ballot(valid[j] && key[j] > thr));
-  const int need_eq = k - gt;
-  int eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const bool eq = valid[j] && key[j] == thr;
-    const uint64_t em = __ballot(eq);
-    const int eq_rank = eq_seen + popc64(em & below);
-    eq_seen += popc64(em);
-    sel[j] = (valid[j] && key[j] > thr) || (eq && eq_rank < need_eq);
-  }
+  select_at<KPL>(key, valid, k, below, thr, exact, sel);
 }
 
 template <int KPL, int RW>
@@ -504,14 +540,9 @@ __global__ __launch_bounds__(256) void select_ranges_kernel(const double* scores
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged rows (exactly 64*KPL keys, no parent list): a workgroup per 16
-// rows of one head, four per wave, four workgroups per CU.  The key means are
-// read once per workgroup: chunks of 4 channels x all keys go from global
-// memory straight into LDS (double-buffered, 16 KB each, one barrier per
-// chunk), and the four waves take their key values from there; every key
-// value feeds four rows.  (Eight rows per wave, 8-channel chunks and two
-// workgroups per CU measured 11% slower: fewer waves to hide the latency.)
-// The two-pass kernel below keeps the 8-channel chunks (SEL_CH).
+// Key means staged in LDS.  The two-pass kernel below streams chunks of
+// SEL_CH channels x PART keys; the single-launch pool-and-select kernel
+// chunks of LDS_CH channels x 512 keys, SEL_RW rows per wave.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int SEL_CH = 8;  // channels per staged chunk
@@ -520,108 +551,138 @@ constexpr int SEL_BYTES = SEL_CH * 8 * 64 * 8;  // 8 channels x 512 keys of floa
 __shared__ __attribute__((aligned(16))) uint8_t s_sel0[SEL_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t s_sel1[SEL_BYTES];
 
-constexpr int LDS_CH = 4;                        // channels per staged chunk (LDS-staged rows)
+constexpr int LDS_CH = 4;                        // channels per staged chunk (single launch)
 constexpr int LDS_BYTES = LDS_CH * 8 * 64 * 8;   // 4 channels x 512 keys of float64
-__shared__ __attribute__((aligned(16))) uint8_t s_lds0[LDS_BYTES];
-__shared__ __attribute__((aligned(16))) uint8_t s_lds1[LDS_BYTES];
+constexpr int SEL_RW = 4;                        // rows per wave (single launch)
 
-constexpr int SEL_RW = 4;  // rows per wave (LDS-staged rows)
+// ---------------------------------------------------------------------------
+// 512 candidates (no parent list) on the float64 matrix core
+// (v_mfma_f64_16x16x4f64: C[16x16] += A[16x4] B[4x16]).  A workgroup of 4 waves
+// takes 16 rows of one (batch, query head); wave w owns the keys
+// [128w, 128w + 128) as 8 tiles of 16 and copies exactly its own quarter of each
+// chunk of 4 channels into LDS (16-byte copies straight to LDS, two buffers),
+// so the walk over the channels needs no workgroup barrier: a wave waits only
+// for its own copies.  Each 4 KB channel row of a chunk is followed by 128
+// bytes of padding, which puts the two channel rows that a half-wave reads on
+// different banks.  For matrix step s the A operand of lane l is
+// q[row l%16][4s + l/16] (a vector load issued a chunk ahead), the B operand
+// K^T[4s + l/16][key 16u + l%16], and lane l receives the scores of rows
+// l/16 + 4r (r = 0..3) at key 16u + l%16.  After the walk the scores go through
+// LDS, 8 rows at a time, and each wave takes the top-k of 2 of them, with the
+// candidates in the order wave_topk expects (lane + 64j).  The float64 products
+// are the ones the vector path forms; only the order of the additions differs.
+// Against the vector path (64 FMAs per 8 doubles read from LDS, the products
+// issued by the vector unit) the matrix core reads a quarter of the LDS bytes
+// per product and leaves the vector and scalar units free.
+// ---------------------------------------------------------------------------
+constexpr int MS_CH = 4;                                  // channels per chunk (one step)
+constexpr int MS_ROW = 4096 + 128;                        // bytes per padded channel row
+constexpr int MS_BUF = MS_CH * MS_ROW;                    // one chunk
+constexpr int MS_SC = 512 + 8;                            // doubles per score row in the exchange
+constexpr int MS_LDS = 2 * MS_BUF > 8 * MS_SC * 8 ? 2 * MS_BUF : 8 * MS_SC * 8;
+__shared__ __attribute__((aligned(16))) uint8_t s_ms[MS_LDS];
 
-// chunk of LDS_CH channels x 512 keys into buffer P (16 B per lane per copy)
+// this wave's quarter of chunk `src` (4 channel rows of 512 keys) into buffer P
 template <int P>
-__device__ __forceinline__ void lds_dma(const double* src) {
-  uint8_t* dst = P ? s_lds1 : s_lds0;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void ms_dma(const double* src, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < LDS_BYTES / 4096; ++i)
-    __builtin_amdgcn_global_load_lds(src + (i * 4096 + tid * 16) / 8,
-                                     (lds_void*)(dst + i * 4096 + wave * 1024), 16, 0, 0);
+  for (int i = 0; i < MS_CH; ++i)
+    __builtin_amdgcn_global_load_lds(src + i * 512 + wave * 128 + lane * 2,
+                                     (lds_void*)(s_ms + P * MS_BUF + i * MS_ROW + wave * 1024), 16, 0, 0);
 }
 
-template <int KPL, int P>
-__device__ __forceinline__ void sel_chunk(const double* const* qp, int c0, double (*acc)[KPL]) {
-  const double* kc = reinterpret_cast<const double*>(P ? s_lds1 : s_lds0);
-  const int lane = threadIdx.x & 63;
-#pragma unroll 2
-  for (int cc = 0; cc < LDS_CH; ++cc) {
-    double kv[KPL];
+// the 8 B operands of this wave for the chunk in buffer P
+template <int P>
+__device__ __forceinline__ void ms_read_b(double (&bv)[8], int wave, int lane) {
+  const double* kc = reinterpret_cast<const double*>(s_ms + P * MS_BUF + (lane >> 4) * MS_ROW) +
+                     wave * 128 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) kv[j] = kc[cc * KPL * 64 + lane + 64 * j];
-#pragma unroll
-    for (int i = 0; i < SEL_RW; ++i) {
-      const double qv = uniform_ld(qp[i] + c0 + cc);
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) acc[i][j] = __builtin_fma(qv, kv[j], acc[i][j]);
-    }
-  }
+  for (int u = 0; u < 8; ++u) bv[u] = kc[16 * u];
 }
 
-template <int KPL>
-__global__ __launch_bounds__(256, 4) void select_lds_kernel(SelArgs a, int64_t groups) {
+__global__ __launch_bounds__(256, 4) void select_mfma_kernel(SelArgs a, int64_t groups) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
   const int64_t rg = unit % groups;
   const int h = (int)((unit / groups) % a.heads_q);
   const int b = (int)(unit / (groups * a.heads_q));
-  const int64_t row0 = (rg * 4 + wave) * SEL_RW;
+  const int64_t row0 = rg * 16;
   const int hk = h / a.group;
-  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * a.keys;
+  const double* kt = a.kt + ((int64_t)b * a.heads_kv + hk) * a.d * 512;
 
-  const double* qp[SEL_RW];
+  // A operand row (a row past the end, or a row map entry outside q, reads row 0)
+  int64_t qr = row0 + (lane & 15);
+  qr = qr < a.rows ? qr : 0;
+  if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + qr];
+  if (qr < 0 || qr >= a.q_len) qr = 0;
+  const double* qa = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d + (lane >> 4);
+  f64x4_sel acc[8];
 #pragma unroll
-  for (int i = 0; i < SEL_RW; ++i) {
-    int64_t qr = row0 + i < a.rows ? row0 + i : (row0 < a.rows ? row0 : 0);
-    if (a.q_rows) qr = a.q_rows[(int64_t)b * a.rows + qr];
-    if (qr < 0 || qr >= a.q_len) qr = 0;  // a row map entry outside q reads row 0
-    qr = __builtin_amdgcn_readfirstlane((int)qr);
-    qp[i] = a.q + (((int64_t)b * a.heads_q + h) * a.q_len + qr) * a.d;
-  }
-  double acc[SEL_RW][KPL];
-#pragma unroll
-  for (int i = 0; i < SEL_RW; ++i)
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) acc[i][j] = 0.0;
+  for (int u = 0; u < 8; ++u) acc[u] = f64x4_sel{0.0, 0.0, 0.0, 0.0};
 
-  // chunks of LDS_CH channels; head_dim / LDS_CH is even (checked at launch)
-  const int n_chunk = a.d / LDS_CH;
-  const int64_t chunk_elems = (int64_t)LDS_CH * a.keys;
-  lds_dma<0>(kt);
+  // chunks of 4 channels, head_dim / 4 even (checked at launch); chunk c + 1 is
+  // copied while chunk c is multiplied
+  const int n_chunk = a.d / MS_CH;
+  double bv[8];
+  ms_dma<0>(kt, wave, lane);
+  double av = qa[0];
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int k = 0; k < n_chunk; k += 2) {
-    lds_dma<1>(kt + (k + 1) * chunk_elems);
-    sel_chunk<KPL, 0>(qp, k * LDS_CH, acc);
+  for (int c = 0; c < n_chunk; c += 2) {
+    ms_dma<1>(kt + (c + 1) * MS_CH * 512, wave, lane);
+    const double an = qa[(c + 1) * MS_CH];
+    ms_read_b<0>(bv, wave, lane);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv[u], acc[u], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the products stay ahead of the wait for the copies
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (k + 2 < n_chunk) lds_dma<0>(kt + (k + 2) * chunk_elems);
-    sel_chunk<KPL, 1>(qp, (k + 1) * LDS_CH, acc);
+    if (c + 2 < n_chunk) {
+      ms_dma<0>(kt + (c + 2) * MS_CH * 512, wave, lane);
+      av = qa[(c + 2) * MS_CH];
+    }
+    ms_read_b<1>(bv, wave, lane);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(an, bv[u], acc[u], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the chunk buffers, which now hold scores
 
+  double* sc = reinterpret_cast<double*>(s_ms);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int i = 0; i < SEL_RW; ++i) {
-    const int64_t row = row0 + i;
-    if (row >= a.rows) continue;
-    uint64_t key[KPL];
-    bool valid[KPL], sel[KPL];
+  for (int half = 0; half < 2; ++half) {
+    // rows 8half .. 8half + 7: lane l holds rows l/16 + 4r for r = 2half, 2half + 1
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      valid[j] = true;
-      key[j] = ordered_key(acc[i][j]);
-    }
-    wave_topk<KPL>(key, valid, a.topk, below, sel);
-    int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row) * a.topk;
-    int base = 0;
+    for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const uint64_t m = __ballot(sel[j]);
-      if (sel[j]) out[base + popc64(m & below)] = lane + 64 * j;
-      base += popc64(m);
+      for (int u = 0; u < 8; ++u)
+        sc[((lane >> 4) + 4 * rr) * MS_SC + wave * 128 + 16 * u + (lane & 15)] = acc[u][2 * half + rr];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r8 = 2 * wave + i;  // row within the 8
+      const int64_t row = row0 + 8 * half + r8;
+      if (row < a.rows) {  // wave-uniform
+        uint64_t key[8];
+        bool valid[8], sel[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          valid[j] = true;
+          key[j] = ordered_key(sc[r8 * MS_SC + lane + 64 * j]);
+        }
+        wave_topk<8>(key, valid, a.topk, below, sel);
+        int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.rows + row) * a.topk;
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint64_t m = __ballot(sel[j]);
+          if (sel[j]) out[base + popc64(m & below)] = lane + 64 * j;
+          base += popc64(m);
+        }
+      }
     }
+    __syncthreads();  // the next 8 rows overwrite the exchange
   }
 }
 
@@ -1206,10 +1267,10 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   if (kpl <= 1) return one_row ? launch_kr<1, 1>(a, d->batch, s) : launch_kr<1, 4>(a, d->batch, s);
   if (kpl <= 2) return one_row ? launch_kr<2, 1>(a, d->batch, s) : launch_kr<2, 4>(a, d->batch, s);
   if (kpl <= 4) return one_row ? launch_kr<4, 1>(a, d->batch, s) : launch_kr<4, 4>(a, d->batch, s);
-  if (!d->parent && a.keys == 512 && a.d % (2 * LDS_CH) == 0) {  // LDS-staged key means
-    const int64_t groups = (a.rows + 4 * SEL_RW - 1) / (4 * SEL_RW);
+  if (!d->parent && a.keys == 512 && a.d % (2 * MS_CH) == 0) {  // float64 matrix core
+    const int64_t groups = (a.rows + 15) / 16;
     dim3 grid((unsigned)(groups * a.heads_q * d->batch), 1);
-    select_lds_kernel<8><<<grid, 256, 0, s>>>(a, groups);
+    select_mfma_kernel<<<grid, 256, 0, s>>>(a, groups);
     return hipGetLastError();
   }
   if (kpl > 4 && kpl <= 8 && !d->parent && a.d % 4 == 0) {  // channel-split rows

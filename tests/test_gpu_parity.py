@@ -181,6 +181,36 @@ def test_select_channel_split_rows(basa, keys, d, row_map):
     assert np.array_equal(host(idx), ref)
 
 
+@pytest.mark.parametrize("case", ["tiled", "wide_range", "infinite"])
+def test_select_512_threshold_search(basa, case):
+    # 512 candidates run the matrix-core kernel (scores exchanged through LDS, then
+    # the bit search for the threshold): equal scores in groups of 8 on both sides
+    # of every threshold, scores spread over hundreds of binades, and rows holding
+    # +inf and -inf scores (40 rows: two full 16-row groups and a ragged one)
+    note(f"select 512 keys, threshold search: {case}")
+    g = np.random.Generator(np.random.PCG64(31))
+    qf = g.standard_normal((1, 2, 40, 128))
+    kbar = g.standard_normal((1, 2, 512, 128))
+    if case == "tiled":
+        kbar = np.tile(kbar[:, :, :64], (1, 1, 8, 1))
+    elif case == "wide_range":
+        kbar *= np.exp(g.uniform(-300.0, 300.0, size=(1, 2, 512, 1)))
+    else:
+        qf[:, :, :, 0] = 4.0
+        kbar[:, :, 5, 0] = 1e308
+        kbar[:, :, 9, 0] = -1e308
+        kbar[:, :, 300, 0] = 1e308
+    qt, kt = dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2)))
+    for topk in (1, 60, 64, 128, 200, 511):
+        out = torch.empty(1, 2, 40, topk, dtype=torch.int32, device="cuda")
+        basa.basa_select(qt, kt, out, topk, scale=1 / math.sqrt(128))
+        torch.cuda.synchronize()
+        ref = orc.topk_ascending(orc.block_logits(qf, kbar, 1 / math.sqrt(128)), topk)
+        assert np.array_equal(host(out), ref), topk
+    if case == "infinite":
+        assert np.isinf(orc.block_logits(qf, kbar, 1.0)[..., [5, 9]]).all()
+
+
 def test_select_children_of_parent_picks(basa):
     note("select candidate mode: 256 rows, parent top-8 x fanout 16")
     g = np.random.Generator(np.random.PCG64(17))
