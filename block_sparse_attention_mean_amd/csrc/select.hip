@@ -142,18 +142,19 @@ __device__ __forceinline__ void wave_topk(const uint64_t* key, const bool* valid
   const uint64_t diff = hi ^ lo;
   const int top = diff ? 63 - __clzll(diff) : -1;
   uint64_t thr = top >= 63 ? 0 : (hi >> (top + 1)) << (top + 1);
-  bool exact = false;
-  for (int bit = top; bit >= 0; --bit) {
+  // The loop leaves with bit >= 0 exactly when a count hit k, so no flag is
+  // carried through it (a flag set before a break costs the loop a round trip
+  // through the vector unit per bit).
+  int bit = top;
+  for (; bit >= 0; --bit) {
     const uint64_t t = thr | (1ull << bit);
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) cnt += popc64(__ballot(valid[j] && key[j] >= t));
-    if (cnt >= k) {
-      thr = t;
-      if (cnt == k) { exact = true; break; }
-    }
+    if (cnt >= k) thr = t;
+    if (cnt == k) break;
   }
-  select_at<KPL>(key, valid, k, below, thr, exact, sel);
+  select_at<KPL>(key, valid, k, below, thr, bit >= 0, sel);
 }
 
 template <int KPL, int RW>
