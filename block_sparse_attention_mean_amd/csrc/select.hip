@@ -571,9 +571,9 @@ constexpr int SEL_RW = 4;                        // rows per wave (single launch
 // l/16 + 4r (r = 0..3) at key 16u + l%16.  After the walk the scores go through
 // LDS, 8 rows at a time, and each wave takes the top-k of 2 of them, with the
 // candidates in the order wave_topk expects (lane + 64j).  The float64 products
-// are the ones the vector path forms; only the order of the additions differs.
-// Against the vector path (64 FMAs per 8 doubles read from LDS, the products
-// issued by the vector unit) the matrix core reads a quarter of the LDS bytes
+// are those of a plain dot product; only the order of the additions differs.
+// Against scoring with vector FMAs (64 FMAs per 8 doubles read from LDS, four
+// rows sharing each key value) the matrix core reads a quarter of the LDS bytes
 // per product and leaves the vector and scalar units free.
 // ---------------------------------------------------------------------------
 constexpr int MS_CH = 4;                                  // channels per chunk (one step)
@@ -692,8 +692,8 @@ __global__ __launch_bounds__(256, 4) void select_mfma_kernel(SelArgs a, int64_t 
 // parent list, top-k <= 256).  The candidates are cut into parts of PART keys.
 // Pass 1: a workgroup takes one part for up to 4*PRW rows that read the same key
 // head (the rows of the query heads of one group, head-major), streams the
-// part's transposed means through LDS in 8-channel chunks (as the LDS-staged
-// kernel does), and writes each row's top-k of the part, in ascending key
+// part's transposed means through LDS in 8-channel chunks (every wave reads
+// every key of a chunk), and writes each row's top-k of the part, in ascending key
 // order, to the workspace (empty slots: candidate -1).  Pass 2: a workgroup
 // per row takes the top-k of the parts' survivors, which are in ascending key
 // order part after part (in two steps, below).  A key in the row's top-k is in
@@ -993,7 +993,8 @@ __global__ __launch_bounds__(256) void select_change_kernel(const T* __restrict_
 // Pooling and selection in one persistent launch (basa_pool_select): the key
 // means of a key head are pooled by key tasks; a selection task pools its own
 // 16 query blocks into LDS, waits until its key head's means are complete,
-// then scores and selects as the LDS-staged kernel above does.  Tasks are
+// then scores its rows with vector FMAs over 4-channel LDS chunks and selects
+// with wave_topk.  Tasks are
 // taken from one ticket counter in this order, per batch: stage s holds the
 // key tasks of key head s/group (at its first query head) and the selection
 // tasks of query head s - PS_LAG, so a selection task is taken after every
