@@ -213,6 +213,29 @@ def test_select_512_threshold_search(basa, case):
             assert np.isinf(orc.block_logits(qf, kbar, 1.0)[..., [5, 9]]).all()
 
 
+@pytest.mark.parametrize("d,row_map", [(32, True), (64, False), (128, True)])
+def test_select_512_batches_groups_and_row_map(basa, d, row_map):
+    # the 512-candidate kernel with batch 2, 6 query heads over 3 key heads, 21
+    # rows (one full 16-row group and a ragged one) and a row map that repeats
+    # and skips query rows; head_dim 32 gives 8 chunks of 4 channels
+    note(f"select 512 keys: batch 2, GQA 6/3, 21 rows, d {d}, row map {row_map}")
+    g = np.random.Generator(np.random.PCG64(40 + d))
+    q_len = 30 if row_map else 21
+    qf = g.standard_normal((2, 6, q_len, d))
+    kbar = g.standard_normal((2, 3, 512, d))
+    rows = None
+    if row_map:
+        rows = np.stack([np.sort(g.choice(q_len, 21, replace=False)) for _ in range(2)]).astype(np.int32)
+        rows[1, 4] = rows[1, 3]
+    idx = torch.empty(2, 6, 21, 64, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, 64,
+                     scale=1 / math.sqrt(d), q_rows=dev(rows) if row_map else None)
+    torch.cuda.synchronize()
+    qsel = np.stack([qf[b][:, rows[b]] for b in range(2)]) if row_map else qf
+    ref = orc.topk_ascending(orc.block_logits(qsel, kbar, 1 / math.sqrt(d)), 64)
+    assert np.array_equal(host(idx), ref)
+
+
 def test_select_children_of_parent_picks(basa):
     note("select candidate mode: 256 rows, parent top-8 x fanout 16")
     g = np.random.Generator(np.random.PCG64(17))
