@@ -236,6 +236,32 @@ def test_select_512_batches_groups_and_row_map(basa, d, row_map):
     assert np.array_equal(host(idx), ref)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_select_512_random_shapes(basa, seed):
+    # seeded shapes for the 512-candidate kernel: head_dim 8..512 (multiples of 8),
+    # batch 1-3, 1-4 key heads with 1-3 query heads each, 1-70 rows, top-k 1-512,
+    # with and without a row map
+    g = np.random.Generator(np.random.PCG64(500 + seed))
+    d = int(g.choice([8, 16, 24, 40, 64, 96, 128, 256, 512]))
+    batch, hkv, group = int(g.integers(1, 4)), int(g.integers(1, 5)), int(g.integers(1, 4))
+    rows, topk, row_map = int(g.integers(1, 71)), int(g.integers(1, 513)), bool(g.integers(0, 2))
+    note(f"select 512 keys random shape {seed}: B{batch} Hkv{hkv} g{group} rows {rows} d {d} "
+         f"top-{topk} row map {row_map}")
+    q_len = rows + 7 if row_map else rows
+    qf = g.standard_normal((batch, hkv * group, q_len, d))
+    kbar = g.standard_normal((batch, hkv, 512, d))
+    rmap = None
+    if row_map:
+        rmap = np.stack([g.integers(0, q_len, rows) for _ in range(batch)]).astype(np.int32)
+    idx = torch.empty(batch, hkv * group, rows, topk, dtype=torch.int32, device="cuda")
+    basa.basa_select(dev(qf), dev(np.ascontiguousarray(np.swapaxes(kbar, -1, -2))), idx, topk,
+                     scale=1 / math.sqrt(d), q_rows=dev(rmap) if row_map else None)
+    torch.cuda.synchronize()
+    qsel = np.stack([qf[b][:, rmap[b]] for b in range(batch)]) if row_map else qf
+    ref = orc.topk_ascending(orc.block_logits(qsel, kbar, 1 / math.sqrt(d)), topk)
+    assert np.array_equal(host(idx), ref)
+
+
 def test_select_children_of_parent_picks(basa):
     note("select candidate mode: 256 rows, parent top-8 x fanout 16")
     g = np.random.Generator(np.random.PCG64(17))
