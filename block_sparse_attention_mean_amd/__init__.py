@@ -28,7 +28,8 @@ EXPORTS = ("basa_status_string", "basa_version", "basa_pool", "basa_select", "ba
            "basa_select_static", "basa_pool_select", "basa_pool_select_workspace", "basa_attn",
            "basa_attn_workspace",
            "basa_merge", "basa_rank_workspace", "basa_rank", "basa_permute", "basa_pool_moments",
-           "basa_block_mass", "basa_block_mass_workspace", "basa_select_ranges", "basa_block_radius")
+           "basa_block_mass", "basa_block_mass_workspace", "basa_select_ranges", "basa_block_radius",
+           "basa_pool_pyramid")
 
 
 class BasaError(RuntimeError):
@@ -50,6 +51,16 @@ class SelectDesc(ctypes.Structure):
 
 
 MAX_SEGMENTS = 4
+PYRAMID_MAX_LEVELS, PYRAMID_MAX_TENSORS = 4, 3
+
+
+class PyramidLevel(ctypes.Structure):
+    _fields_ = [("mean_rows", ctypes.c_void_p), ("mean_cols", ctypes.c_void_p),
+                ("mean_copy", ctypes.c_void_p)]
+
+
+class PyramidTensor(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("level", PyramidLevel * PYRAMID_MAX_LEVELS)]
 
 
 class KvSegment(ctypes.Structure):
@@ -84,6 +95,9 @@ def _load() -> ctypes.CDLL:
     lib.basa_version.argtypes = []
     lib.basa_pool.restype = i32
     lib.basa_pool.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i32, vp]
+    lib.basa_pool_pyramid.restype = i32
+    lib.basa_pool_pyramid.argtypes = [ctypes.POINTER(PyramidTensor), i32, i32, i64, i64, i64, i64,
+                                      i32, i32, vp]
     lib.basa_select.restype = i32
     lib.basa_select.argtypes = [ctypes.POINTER(SelectDesc), vp, vp, i32, vp, vp]
     lib.basa_pool_select.restype = i32
@@ -188,6 +202,52 @@ def prepare_pool(x: torch.Tensor, block: int, mean_rows: torch.Tensor | None = N
     args = (_ptr(x), _dt(x), outer, length, d, block, _ptr(mean_rows), _ptr(mean_cols),
             _ptr(mean_copy), copy_dt)
     return _prepared("basa_pool", lib.basa_pool, args, (x, mean_rows, mean_cols, mean_copy))
+
+
+def basa_pool_pyramid(xs, block: int, outputs) -> None:
+    """The log-linear pooling pyramid of up to three tensors (see prepare_pool_pyramid)."""
+    prepare_pool_pyramid(xs, block, outputs)()
+
+
+def prepare_pool_pyramid(xs, block: int, outputs):
+    """basa_pool_pyramid validated once.  xs: 1-3 tensors [..., len, head_dim] of one shape and
+    dtype; outputs[i][l] = (mean_rows, mean_cols, mean_copy) of level l + 1 of xs[i], None where
+    absent (mean_rows [..., n_l, head_dim] float64, mean_cols [..., head_dim, n_l] float64,
+    mean_copy [..., n_l, head_dim] float32 or bf16, n_l = len / block^(l+1))."""
+    n = len(xs)
+    if not 1 <= n <= PYRAMID_MAX_TENSORS or len(outputs) != n:
+        raise ValueError(f"1 to {PYRAMID_MAX_TENSORS} tensors, one output list each")
+    levels = len(outputs[0])
+    if not 1 <= levels <= PYRAMID_MAX_LEVELS:
+        raise ValueError(f"1 to {PYRAMID_MAX_LEVELS} levels")
+    *lead, length, d = xs[0].shape
+    outer = 1
+    for s in lead:
+        outer *= s
+    arr = (PyramidTensor * n)()
+    copy_dts = set()
+    for i, x in enumerate(xs):
+        if x.shape != xs[0].shape or x.dtype != xs[0].dtype:
+            raise ValueError("pyramid inputs must share shape and dtype")
+        if len(outputs[i]) != levels:
+            raise ValueError("every tensor needs the same number of levels")
+        arr[i].x = _ptr(x)
+        span = 1
+        for lv, (rows, cols, copy) in enumerate(outputs[i]):
+            span *= block
+            if block > 0 and length % span == 0:   # otherwise the C call reports BASA_E_SHAPE
+                nb = length // span
+                _shape("mean_rows", rows, (*lead, nb, d))
+                _shape("mean_cols", cols, (*lead, d, nb))
+                _shape("mean_copy", copy, (*lead, nb, d))
+            if copy is not None:
+                copy_dts.add(_dt(copy))
+            arr[i].level[lv] = PyramidLevel(_ptr(rows), _ptr(cols), _ptr(copy))
+    if len(copy_dts) > 1:
+        raise ValueError("every mean_copy of one pyramid call must have the same dtype")
+    copy_dt = copy_dts.pop() if copy_dts else F32
+    args = (arr, n, _dt(xs[0]), outer, length, d, block, levels, copy_dt)
+    return _prepared("basa_pool_pyramid", lib.basa_pool_pyramid, args, (xs, outputs, arr))
 
 
 def _prepared(name, fn, args, keep):
@@ -598,7 +658,8 @@ def basa_permute(x: torch.Tensor, perm: torch.Tensor, out: torch.Tensor,
                                             mode, _ptr(out), _stream()))
 
 
-__all__ = ["basa_pool", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn",
+__all__ = ["basa_pool", "basa_pool_pyramid", "prepare_pool_pyramid", "PyramidLevel", "PyramidTensor",
+           "PYRAMID_MAX_LEVELS", "PYRAMID_MAX_TENSORS", "basa_select", "basa_select_workspace", "basa_select_static", "basa_attn",
            "basa_pool_select", "basa_pool_select_workspace", "prepare_pool_select",
            "basa_attn_workspace", "prepare_attn", "prepare_pool", "prepare_select", "prepare_merge", "basa_merge", "kv_segment", "BasaError", "lib",
            "LIB_PATH", "EXPORTS", "SelectDesc", "AttnDesc", "KvSegment", "MAX_SEGMENTS", "F32", "BF16", "F64", "SELECT_BLOCKS",

@@ -58,6 +58,45 @@ int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t he
   }
 }
 
+int basa_pool_pyramid(const basa_pyramid_tensor* tensors, int n_tensors, int x_dtype,
+                      int64_t outer, int64_t len, int64_t head_dim, int64_t block, int levels,
+                      int copy_dtype, void* stream) {
+  try {
+    if (!tensors) return BASA_E_NULLPTR;
+    if (n_tensors < 1 || n_tensors > BASA_PYRAMID_MAX_TENSORS) return BASA_E_SHAPE;
+    if (levels < 1 || levels > BASA_PYRAMID_MAX_LEVELS) return BASA_E_SHAPE;
+    if (outer < 0 || len < 0 || block < 2 || block > 32) return BASA_E_SHAPE;
+    if (head_dim < 8 || head_dim > 512 || head_dim % 8 != 0 || block * head_dim > 4096)
+      return BASA_E_SHAPE;
+    int64_t span = 1;
+    for (int l = 0; l < levels; ++l) span *= block;
+    if (len % span != 0) return BASA_E_SHAPE;
+    if (x_dtype != BASA_F32 && x_dtype != BASA_BF16 && x_dtype != BASA_F64) return BASA_E_DTYPE;
+    bool any_copy = false;
+    for (int i = 0; i < n_tensors; ++i)
+      for (int l = 0; l < levels; ++l) any_copy = any_copy || tensors[i].level[l].mean_copy;
+    if (any_copy && copy_dtype != BASA_F32 && copy_dtype != BASA_BF16) return BASA_E_DTYPE;
+    if (outer * len == 0) return BASA_OK;
+    for (int i = 0; i < n_tensors; ++i) {
+      const basa_pyramid_tensor& t = tensors[i];
+      if (!t.x) return BASA_E_NULLPTR;
+      if (!aligned16(t.x)) return BASA_E_ALIGN;
+      for (int l = 0; l < levels; ++l) {
+        const basa_pyramid_level& v = t.level[l];
+        if (!v.mean_rows && !v.mean_cols && !v.mean_copy) return BASA_E_NULLPTR;
+        if (l >= 1 && l + 1 < levels && !v.mean_rows) return BASA_E_NULLPTR;  // read by level l+2
+        if (!aligned16(v.mean_rows) || !aligned16(v.mean_cols) || !aligned16(v.mean_copy))
+          return BASA_E_ALIGN;
+      }
+    }
+    return from_hip(basa::launch_pool_pyramid(tensors, n_tensors, x_dtype, outer, len, head_dim,
+                                              block, levels, copy_dtype,
+                                              static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return BASA_E_LAUNCH;
+  }
+}
+
 int basa_pool_moments(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                       int64_t block, int role, double scale, double beta, double* out,
                       void* stream) {

@@ -75,6 +75,9 @@ template <> struct Vec8<uint16_t> {
 hipError_t launch_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
                        int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
                        int copy_dtype, hipStream_t s);
+hipError_t launch_pool_pyramid(const basa_pyramid_tensor* t, int n_t, int x_dtype, int64_t outer,
+                               int64_t len, int64_t head_dim, int64_t block, int levels,
+                               int copy_dtype, hipStream_t s);
 hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, const double* kt,
                                 int32_t* idx, hipStream_t s);
 int64_t select_workspace_bytes(const basa_select_desc* d);

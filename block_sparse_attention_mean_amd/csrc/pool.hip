@@ -185,6 +185,107 @@ __global__ __launch_bounds__(256) void pool_short_kernel(const T* __restrict__ x
   }
 }
 
+// ---------------------------------------------------------------------------
+// The log-linear pyramid (log-linear README: each level pools the level below
+// by `block`).  Levels 1 and 2 of every tensor in one launch: a workgroup
+// takes one level-2 block of one tensor (blockIdx.y), one thread per (level-1
+// block, 8-channel group) adds that block's rows in row order with all of
+// them in flight, keeps the mean in LDS, and then one thread per channel adds
+// the `block` level-1 means in block order.  Further levels: one thread per
+// (block, 8-channel group) of every tensor, from the level below's float64
+// means.  The sums run in the order pool_short_kernel uses, so every level
+// equals a chain of single-level pooling calls bit for bit.
+// ---------------------------------------------------------------------------
+struct PyrLevel {
+  double* rows;
+  double* cols;
+  void* copy;
+};
+struct PyrArgs {
+  const void* x[BASA_PYRAMID_MAX_TENSORS];
+  PyrLevel lv[BASA_PYRAMID_MAX_TENSORS][BASA_PYRAMID_MAX_LEVELS];
+  int64_t outer, len;
+  int d, block, copy_dtype;
+};
+constexpr int PYR_RED = 4096;  // doubles of level-1 means per workgroup (block * head_dim)
+
+__device__ __forceinline__ void pyr_put(const PyrLevel& out, int64_t o, int64_t nb, int64_t g, int d,
+                                        int c, double mean, int copy_dtype) {
+  if (out.rows) out.rows[(o * nb + g) * d + c] = mean;
+  if (out.cols) out.cols[(o * d + c) * nb + g] = mean;
+  if (out.copy) {
+    if (copy_dtype == BASA_F32)
+      reinterpret_cast<float*>(out.copy)[(o * nb + g) * d + c] = (float)mean;
+    else
+      reinterpret_cast<uint16_t*>(out.copy)[(o * nb + g) * d + c] = f64_to_bf16_bits(mean);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pyramid12_kernel(PyrArgs a) {
+  __shared__ double red[PYR_RED];
+  const int tn = blockIdx.y;
+  const int d = a.d, block = a.block, cols8 = d >> 3;
+  const int64_t nb1 = a.len / block, nb2 = nb1 / block;
+  const int64_t o = blockIdx.x / nb2, g2 = blockIdx.x - o * nb2;
+  const T* x = static_cast<const T*>(a.x[tn]);
+  for (int item = threadIdx.x; item < block * cols8; item += blockDim.x) {
+    const int b1 = item / cols8, c8 = item - b1 * cols8;
+    const int64_t g1 = g2 * block + b1;
+    const T* src = x + (o * a.len + g1 * block) * d + c8 * 8;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int r = 0;
+    // NB rows in flight (64 registers of raw data), then their adds in row order
+    constexpr int NB = sizeof(T) == 2 ? 16 : (sizeof(T) == 4 ? 8 : 4);
+    for (; r + NB <= block; r += NB) {
+      typename Load8<T>::Raw raw[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) raw[u] = Load8<T>::load(src + (int64_t)(r + u) * d);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) Load8<T>::add(raw[u], acc);
+    }
+    for (; r < block; ++r) Load8<T>::add(Load8<T>::load(src + (int64_t)r * d), acc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double mean = acc[i] / (double)block;
+      pyr_put(a.lv[tn][0], o, nb1, g1, d, c8 * 8 + i, mean, a.copy_dtype);
+      red[b1 * d + c8 * 8 + i] = mean;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    double sum = 0.0;
+    for (int r = 0; r < block; ++r) sum += red[r * d + c];
+    pyr_put(a.lv[tn][1], o, nb2, g2, d, c, sum / (double)block, a.copy_dtype);
+  }
+}
+
+// level lv (0-based index, >= 2) from the float64 rows of level lv - 1
+__global__ __launch_bounds__(256) void pyramid_next_kernel(PyrArgs a, int lv, int64_t nb_in, int64_t nb,
+                                                           int64_t n_items) {
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (item >= n_items) return;
+  const int tn = blockIdx.y;
+  const int d = a.d, block = a.block, cols8 = d >> 3;
+  const int c8 = (int)(item % cols8);
+  const int64_t gb = item / cols8;
+  const int64_t o = gb / nb, g = gb - o * nb;
+  const double* src = a.lv[tn][lv - 1].rows + (o * nb_in + g * (int64_t)block) * d + c8 * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int r = 0;
+  for (; r + 8 <= block; r += 8) {
+    typename Load8<double>::Raw raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = Load8<double>::load(src + (int64_t)(r + u) * d);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Load8<double>::add(raw[u], acc);
+  }
+  for (; r < block; ++r) Load8<double>::add(Load8<double>::load(src + (int64_t)r * d), acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    pyr_put(a.lv[tn][lv], o, nb, g, d, c8 * 8 + i, acc[i] / (double)block, a.copy_dtype);
+}
+
 template <typename T>
 hipError_t launch_typed(const T* x, int64_t outer, int64_t len, int d, int block, double* mean_rows,
                         double* mean_cols, void* mean_copy, int copy_dtype, hipStream_t s) {
@@ -234,6 +335,52 @@ hipError_t launch_pool(const void* x, int x_dtype, int64_t outer, int64_t len, i
       return launch_typed(static_cast<const double*>(x), outer, len, d, b, mean_rows, mean_cols,
                           mean_copy, copy_dtype, s);
   }
+}
+
+hipError_t launch_pool_pyramid(const basa_pyramid_tensor* t, int n_t, int x_dtype, int64_t outer,
+                               int64_t len, int64_t head_dim, int64_t block, int levels,
+                               int copy_dtype, hipStream_t s) {
+  if (outer * len == 0) return hipSuccess;
+  if (levels == 1) {  // one level: the plain pooling call per tensor
+    for (int i = 0; i < n_t; ++i) {
+      const hipError_t e = launch_pool(t[i].x, x_dtype, outer, len, head_dim, block,
+                                       t[i].level[0].mean_rows, t[i].level[0].mean_cols,
+                                       t[i].level[0].mean_copy, copy_dtype, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  PyrArgs a{};
+  for (int i = 0; i < n_t; ++i) {
+    a.x[i] = t[i].x;
+    for (int l = 0; l < levels; ++l)
+      a.lv[i][l] = PyrLevel{t[i].level[l].mean_rows, t[i].level[l].mean_cols, t[i].level[l].mean_copy};
+  }
+  a.outer = outer;
+  a.len = len;
+  a.d = (int)head_dim;
+  a.block = (int)block;
+  a.copy_dtype = copy_dtype;
+  const int64_t nb2 = len / block / block;
+  const int items = (int)(block * (head_dim / 8));
+  const int threads = items >= 256 ? 256 : (items + 63) / 64 * 64;
+  dim3 g12((unsigned)(outer * nb2), (unsigned)n_t);
+  switch (x_dtype) {
+    case BASA_BF16: pyramid12_kernel<uint16_t><<<g12, threads, 0, s>>>(a); break;
+    case BASA_F32: pyramid12_kernel<float><<<g12, threads, 0, s>>>(a); break;
+    default: pyramid12_kernel<double><<<g12, threads, 0, s>>>(a); break;
+  }
+  hipError_t e = hipGetLastError();
+  int64_t nb_in = nb2;
+  for (int l = 2; l < levels && e == hipSuccess; ++l) {
+    const int64_t nb = nb_in / block;
+    const int64_t n_items = outer * nb * (head_dim / 8);
+    dim3 g((unsigned)((n_items + 255) / 256), (unsigned)n_t);
+    pyramid_next_kernel<<<g, 256, 0, s>>>(a, l, nb_in, nb, n_items);
+    e = hipGetLastError();
+    nb_in = nb;
+  }
+  return e;
 }
 
 }  // namespace basa

@@ -29,7 +29,8 @@ import torch
 from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELECT_BLOCKS,
                SELECT_CHANGE, basa_attn, basa_attn_workspace, basa_block_mass,
                basa_block_mass_workspace, basa_merge,
-               basa_permute, basa_pool, basa_pool_moments, basa_rank, basa_rank_workspace,
+               basa_permute, basa_pool, basa_pool_moments, basa_pool_pyramid, basa_rank,
+               basa_rank_workspace,
                basa_select, basa_select_ranges, basa_select_workspace, kv_segment, prepare_attn,
                prepare_merge, prepare_pool, prepare_select)
 
@@ -258,9 +259,10 @@ class LlsaForward:
         for lv in range(1, self.levels + 1):
             nl = n // block ** lv
             self.qm[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
-            self.km[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
             self.kt[lv] = _empty(b, h, d, nl, dtype=f64, like=q)
-            self.vm[lv] = _empty(b, h, nl, d, dtype=f64, like=q)
+            # float64 K and V rows only where the next level is pooled from them
+            self.km[lv] = _empty(b, h, nl, d, dtype=f64, like=q) if 2 <= lv < self.levels else None
+            self.vm[lv] = _empty(b, h, nl, d, dtype=f64, like=q) if 2 <= lv < self.levels else None
             self.kf[lv] = _empty(b, h, nl, d, dtype=f32, like=q)
             self.vf[lv] = _empty(b, h, nl, d, dtype=f32, like=q)
             self.sel[lv] = _empty(b, h, nl, topk, dtype=torch.int32, like=q)
@@ -272,14 +274,13 @@ class LlsaForward:
         self.lse = _empty(b, h, n, dtype=f32, like=q)
 
     def pool(self):
-        bl = self.block
-        for lv in range(1, self.levels + 1):
-            sq = self.q if lv == 1 else self.qm[lv - 1]
-            sk = self.k if lv == 1 else self.km[lv - 1]
-            sv = self.v if lv == 1 else self.vm[lv - 1]
-            basa_pool(sq, bl, mean_rows=self.qm[lv])
-            basa_pool(sk, bl, mean_rows=self.km[lv], mean_cols=self.kt[lv], mean_copy=self.kf[lv])
-            basa_pool(sv, bl, mean_rows=self.vm[lv], mean_copy=self.vf[lv])
+        # every level of Q, K and V in one call (levels 1-2 in one launch, each further
+        # level in one more); the same means as pooling level by level
+        lv = range(1, self.levels + 1)
+        basa_pool_pyramid([self.q, self.k, self.v], self.block,
+                          [[(self.qm[i], None, None) for i in lv],
+                           [(self.km[i], self.kt[i], self.kf[i]) for i in lv],
+                           [(self.vm[i], None, self.vf[i]) for i in lv]])
 
     def select(self):
         top = self.levels

@@ -11,6 +11,8 @@
  *                blocks listed for each query tile; emits O and the LSE
  *   basa_merge   combines two partial (O, LSE) results of one row
  *   basa_select_static  basa_select without a caller workspace (no allocation)
+ *   basa_pool_pyramid  basa_pool repeated level by level (each level pools
+ *                the previous one) for up to three tensors in two launches
  *   basa_pool_moments  block means and variances arranged so that the
  *                covariance-compensated block score is one dot product
  *   basa_block_mass    block mass of the dense attention map
@@ -89,6 +91,56 @@ int basa_version(void);
 int basa_pool(const void* x, int x_dtype, int64_t outer, int64_t len, int64_t head_dim,
               int64_t block, double* mean_rows, double* mean_cols, void* mean_copy,
               int copy_dtype, void* stream);
+
+/* Outputs of one pyramid level of one tensor (any of them may be NULL). */
+typedef struct basa_pyramid_level {
+  double* mean_rows;  /* device, [outer][len/block^l][head_dim] float64 */
+  double* mean_cols;  /* device, [outer][head_dim][len/block^l] float64 */
+  void* mean_copy;    /* device, [outer][len/block^l][head_dim] of copy_dtype */
+} basa_pyramid_level;
+
+#define BASA_PYRAMID_MAX_LEVELS 4
+#define BASA_PYRAMID_MAX_TENSORS 3
+
+/* One input of basa_pool_pyramid and its outputs; level[l-1] is level l. */
+typedef struct basa_pyramid_tensor {
+  const void* x;      /* device, [outer][len][head_dim] of x_dtype */
+  basa_pyramid_level level[BASA_PYRAMID_MAX_LEVELS];
+} basa_pyramid_tensor;
+
+/*
+ * basa_pool_pyramid - the log-linear pooling pyramid.
+ *
+ * Follows the log-linear README (method paragraphs on the hierarchy): level
+ * 1 holds the means of `block` consecutive tokens, and every further level
+ * the means of `block` consecutive entries of the level below.  For each of
+ * the n_tensors inputs and each level l = 1..levels the call writes what
+ * basa_pool(level l-1 -> level l) would write into that level's outputs, bit
+ * for bit: every sum is taken in float64 in the same order (the rows of a
+ * block in ascending order), and level l >= 2 is pooled from the float64
+ * means of level l-1.  Levels 1 and 2 of all tensors take one launch (a
+ * workgroup pools `block` level-1 blocks and then their level-2 block from
+ * LDS), every further level one launch.
+ *
+ *   tensors    host array of n_tensors (1..BASA_PYRAMID_MAX_TENSORS)
+ *              descriptors; all share x_dtype (F32, BF16 or F64), outer,
+ *              len and head_dim
+ *   levels     1..BASA_PYRAMID_MAX_LEVELS; len must be a multiple of
+ *              block^levels
+ *   block      2..32, with block * head_dim <= 4096
+ *   copy_dtype F32 or BF16 (read only where a mean_copy is given)
+ *
+ * Every level of every tensor needs at least one output, and every level
+ * from 2 up to the one below the top its mean_rows (the next level is pooled
+ * from them; level 2 is pooled from level 1 inside the workgroup, so level
+ * 1 needs no float64 rows unless the caller wants them).
+ * Errors: BASA_E_SHAPE for sizes outside the above (head_dim a multiple of 8,
+ * at most 512), BASA_E_NULLPTR for a missing input or required output,
+ * BASA_E_DTYPE, BASA_E_ALIGN.  outer*len == 0 enqueues nothing.
+ */
+int basa_pool_pyramid(const basa_pyramid_tensor* tensors, int n_tensors, int x_dtype,
+                      int64_t outer, int64_t len, int64_t head_dim, int64_t block, int levels,
+                      int copy_dtype, void* stream);
 
 /* Roles of basa_pool_moments. */
 enum {

@@ -69,6 +69,45 @@ def test_pool_validation():
     assert pool(length=0) == OK
 
 
+def pyramid(xs=(FAKE,), levels=2, outs=None, xdt=basa.BF16, outer=2, length=4096, d=64, block=16,
+            cdt=basa.F32, n=None):
+    arr = (basa.PyramidTensor * max(len(xs), 1))()
+    for i, x in enumerate(xs):
+        arr[i].x = x
+        for lv in range(min(levels, basa.PYRAMID_MAX_LEVELS)):
+            rows, cols, copy = (outs or {}).get((i, lv), (FAKE, None, None))
+            arr[i].level[lv] = basa.PyramidLevel(rows, cols, copy)
+    n_t = len(xs) if n is None else n
+    return basa.lib.basa_pool_pyramid(arr, n_t, xdt, outer, length, d, block, levels, cdt, None)
+
+
+def test_pool_pyramid_validation():
+    assert pyramid(length=4000) == SHAPE              # not a multiple of block^levels
+    assert pyramid(length=16 * 24) == SHAPE           # a multiple of block, not of block^2
+    assert pyramid(block=1) == SHAPE
+    assert pyramid(block=33, length=33 * 33) == SHAPE
+    assert pyramid(d=512) == SHAPE                    # block * head_dim above 4096
+    assert pyramid(d=100) == SHAPE
+    assert pyramid(outer=-1) == SHAPE
+    assert pyramid(levels=0) == SHAPE
+    assert pyramid(levels=5, length=16 ** 5) == SHAPE
+    assert pyramid(n=0) == SHAPE
+    assert pyramid(n=4) == SHAPE
+    assert pyramid(xdt=7) == DTYPE
+    assert pyramid(outs={(0, 1): (FAKE, None, FAKE)}, cdt=basa.F64) == DTYPE
+    assert basa.lib.basa_pool_pyramid(None, 1, basa.BF16, 2, 4096, 64, 16, 2, basa.F32,
+                                      None) == NULLPTR
+    assert pyramid(xs=(0,)) == NULLPTR
+    assert pyramid(outs={(0, 1): (None, None, None)}) == NULLPTR   # a level with no output
+    # level 3 is pooled from the rows of level 2 (level 2 from level 1 inside the workgroup)
+    assert pyramid(levels=3, outs={(0, 1): (None, FAKE, None)}) == NULLPTR
+    assert pyramid(xs=(FAKE, 0)) == NULLPTR
+    assert pyramid(xs=(MISALIGNED,)) == ALIGN
+    assert pyramid(outs={(0, 1): (FAKE, MISALIGNED, None)}) == ALIGN
+    assert pyramid(outer=0) == OK                     # empty: nothing to do
+    assert pyramid(length=0) == OK
+
+
 def sel_desc(**kw):
     d = basa.SelectDesc()
     d.mode, d.topk, d.batch, d.heads_q, d.heads_kv = basa.SELECT_BLOCKS, 4, 1, 2, 2

@@ -90,6 +90,64 @@ def test_pool_f64_levels_and_copies(basa):
     assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-12))
 
 
+def _pyramid_inputs(case):
+    g = np.random.Generator(np.random.PCG64(31))
+    if case == "bf16_llsa":      # the log-linear shape: Q, K, V, block 16, three levels
+        x = wl.make_dlm(31, heads=3, tokens=16 ** 3, head_dim=64)
+        return [x["q"], x["k"], x["v"]], 16, 3, torch.float32
+    if case == "bf16_copies":    # bf16 copies, two levels, block 8, head_dim 128
+        x = wl.make_dlm(32, heads=2, tokens=8 * 8 * 6, head_dim=128)
+        return [x["k"], x["v"]], 8, 2, torch.bfloat16
+    if case == "f32_ragged":     # float32, block 8 (a partial batch of rows in flight), outer 4
+        return [g.standard_normal((2, 2, 8 * 8 * 5, 24)).astype(np.float32)], 8, 2, torch.float32
+    # float64, block 4, four levels, head_dim 8
+    return [g.standard_normal((1, 1, 4 ** 4 * 3, 8)), g.standard_normal((1, 1, 4 ** 4 * 3, 8))], 4, 4, \
+        torch.float32
+
+
+@pytest.mark.parametrize("case", ["bf16_llsa", "bf16_copies", "f32_ragged", "f64_four_levels"])
+def test_pool_pyramid_equals_chained_pooling(basa, case):
+    """basa_pool_pyramid against basa_pool applied level by level (level l from the float64
+    rows of level l - 1): every output identical bit for bit.  For bf16 inputs every level also
+    equals the oracle's pooled means exactly (float64 sums of bf16 values are exact)."""
+    note(f"pool pyramid {case}")
+    xs, block, levels, copy_dt = _pyramid_inputs(case)
+    ts = [dev(x) for x in xs]
+    *lead, length, d = ts[0].shape
+    outs, refs = [], []
+    for i, t in enumerate(ts):
+        lv_out, lv_ref, src = [], [], t
+        for lv in range(1, levels + 1):
+            nb = length // block ** lv
+            def mk():
+                rows = torch.empty(*lead, nb, d, dtype=torch.float64, device="cuda")
+                cols = torch.empty(*lead, d, nb, dtype=torch.float64, device="cuda") \
+                    if i != 0 or lv == levels else None
+                copy = torch.empty(*lead, nb, d, dtype=copy_dt, device="cuda") if i != 0 else None
+                return rows, cols, copy
+            o, r = mk(), mk()
+            for buf in (*o, *r):
+                if buf is not None:
+                    buf.fill_(float("nan"))
+            basa.basa_pool(src, block, *r)
+            lv_out.append(o)
+            lv_ref.append(r)
+            src = r[0]
+        outs.append(lv_out)
+        refs.append(lv_ref)
+    basa.basa_pool_pyramid(ts, block, outs)
+    torch.cuda.synchronize()
+    for i in range(len(ts)):
+        ref_mean = xs[i]
+        for lv in range(levels):
+            for got, want in zip(outs[i][lv], refs[i][lv]):
+                if got is not None:
+                    assert torch.equal(got, want), (case, i, lv)
+            if case.startswith("bf16"):
+                ref_mean = orc.pool_mean(ref_mean, block)
+                assert np.array_equal(host(outs[i][lv][0]), ref_mean)
+
+
 # --------------------------------------------------------------------------- select
 
 def test_select_tiny_planted_block(basa):
