@@ -7,8 +7,9 @@
 // segments with an additive logit bias per level.  Online softmax per 16-key
 // block.
 //
-// One wave computes one tile; a workgroup holds four waves.  Float32 segments
-// whose list row is shared by the workgroup's four tiles are staged once per
+// One wave computes one tile; a workgroup holds four waves (sixteen for the
+// log-linear levels).  Float32 segments whose list row is shared by the
+// workgroup's tiles are staged once per
 // workgroup (barrier-synchronised); everything else each wave walks alone.  Per 16-key block the wave forms S^T = K Q^T with
 // v_mfma_f32_16x16x16bf16_1k: lane l holds the logits of query row l%16 for
 // keys 4(l/16) .. +3, which is exactly the B operand (P^T) of the next
@@ -29,7 +30,7 @@
 namespace basa {
 namespace {
 
-constexpr int NW = 4;          // waves (tiles) per workgroup
+constexpr int NW = 4;          // waves (tiles) per workgroup (16 for the log-linear coarse levels)
 constexpr float kLazy = 8.0f;  // log2 headroom before the max is raised
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -53,7 +54,7 @@ struct T16Args {
   const int32_t* q_rows;
   int64_t len_q, lists, tiles;
   int heads_q, heads_kv, group;
-  int share;  // lists % NW == 0: the NW tiles of a workgroup share list rows with shift >= 2
+  int share;  // the workgroup's tiles are consecutive tiles of one (batch, head) (lists % tiles per workgroup == 0)
   float scale_log2;
 };
 
@@ -251,20 +252,20 @@ __device__ __forceinline__ void t16_segment(float scale_log2, const T16Seg& sg, 
   }
 }
 
-// A float32 segment whose list row is the same for all NW tiles of the
+// A float32 segment whose list row is the same for all NWT tiles of the
 // workgroup (the log-linear coarse levels): the workgroup walks it together,
-// NW blocks per chunk.  Wave w loads block w of the chunk, splits it into bf16
+// NWT blocks per chunk.  Wave w loads block w of the chunk, splits it into bf16
 // hi/lo and stores keys and values in slot w of the shared LDS area; after a
-// barrier every wave reduces all NW slots for its own rows.  Each coarse block
+// barrier every wave reduces all NWT slots for its own rows.  Each coarse block
 // is thus read and split once per workgroup instead of once per tile.  The
 // next chunk's rows are loaded while the current chunk is reduced.
-template <int D>
+template <int D, int NWT>
 struct T16Shared {
   static constexpr int SLOT = 4 * T16Lds<D>::HALF;  // keys hi, keys lo, values hi, values lo
-  static constexpr int BYTES = NW * SLOT;
+  static constexpr int BYTES = NWT * SLOT;
 };
 
-template <int D>
+template <int D, int NWT>
 __device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Seg& sg,
                                                    const int32_t* lst, int64_t head_row,
                                                    const v4i16* qb, uint8_t* shared,
@@ -282,25 +283,25 @@ __device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Se
     kr.load(sg.k, r * D + ch0);
     vr.load(sg.v, r * D + ch0);
   }
-  for (int c0 = 0; c0 < n; c0 += NW) {
-    uint8_t* slot = shared + wave * T16Shared<D>::SLOT;
+  for (int c0 = 0; c0 < n; c0 += NWT) {
+    uint8_t* slot = shared + wave * T16Shared<D, NWT>::SLOT;
     t16_store_rows<D, false>(kr, slot);
     t16_store_rows<D, false>(vr, slot + 2 * HALF);
     __syncthreads();
-    if (c0 + NW < n) {  // next chunk's rows
-      const int j = c0 + NW + wave;
+    if (c0 + NWT < n) {  // next chunk's rows
+      const int j = c0 + NWT + wave;
       const int64_t rr = j < n ? t16_row(lst, j, sg.len) : -1;
       const int64_t r = head_row + (rr >= 0 ? rr : 0);
       kr.load(sg.k, r * D + ch0);
       vr.load(sg.v, r * D + ch0);
     }
-    for (int b = 0; b < NW; ++b) {
+    for (int b = 0; b < NWT; ++b) {
       const int j = c0 + b;
       if (j >= n) break;
       const int32_t blk = lst[j];
       if (blk < 0) continue;  // an unused list slot (wave-uniform)
       const bool kvalid = (int64_t)blk * 16 + (lane & 15) < sg.len;
-      const uint8_t* ks = shared + b * T16Shared<D>::SLOT + (lane & 15) * T16Lds<D>::STRIDE + ch0 * 2;
+      const uint8_t* ks = shared + b * T16Shared<D, NWT>::SLOT + (lane & 15) * T16Lds<D>::STRIDE + ch0 * 2;
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st_ = 0; st_ < CPL / 4; ++st_) {
@@ -310,26 +311,31 @@ __device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Se
         s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, qb[st_], s, 0, 0, 0);
       }
       t16_softmax_pv<D, true>(s, kvalid, scale_log2, sg.bias_log2,
-                              shared + b * T16Shared<D>::SLOT + 2 * HALF, st);
+                              shared + b * T16Shared<D, NWT>::SLOT + 2 * HALF, st);
     }
     __syncthreads();  // the slots are rewritten by the next chunk
   }
 }
 
 // F32: some segment has a float32 table (without it the float32 path, and its
-// registers, are not compiled in)
-template <bool O_BF16, int D, bool F32>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 3) void attn_t16_kernel(T16Args a) {
+// registers, are not compiled in).  NWT tiles (waves) per workgroup: 4, or 16
+// when the float32 lists repeat over 16 consecutive tiles (the log-linear
+// levels above the first: a level-2 block's 16 tiles share their level-1
+// candidates), so that each coarse block is read and split once per 16 tiles.
+template <bool O_BF16, int D, bool F32, int NWT>
+__global__ __launch_bounds__(NWT * 64, NWT == 16 ? 1 : (D == 64 ? 4 : 3)) void attn_t16_kernel(T16Args a) {
   constexpr int CPL = D / 4;
+  constexpr int SHARE_SHIFT = NWT == 16 ? 4 : 2;  // list rows with this shift repeat over the workgroup
   // per-wave areas; with float32 segments also the shared area, which they alias
   // (the shared segments are done, behind a barrier, before any per-wave area is used)
-  constexpr int SMEM = (F32 && T16Shared<D>::BYTES > NW * T16Lds<D>::BYTES) ? T16Shared<D>::BYTES
-                                                                            : NW * T16Lds<D>::BYTES;
+  constexpr int SMEM = (F32 && T16Shared<D, NWT>::BYTES > NWT * T16Lds<D>::BYTES)
+                           ? T16Shared<D, NWT>::BYTES
+                           : NWT * T16Lds<D>::BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t tile = (int64_t)blockIdx.x * NW + wave;
-  // with a.share the tile count is a multiple of NW, so no wave of a workgroup that
+  const int64_t tile = (int64_t)blockIdx.x * NWT + wave;
+  // with a.share the tile count is a multiple of NWT, so no wave of a workgroup that
   // meets a barrier leaves here
   if (tile >= a.tiles) return;
   uint8_t* lds = smem + wave * T16Lds<D>::BYTES;
@@ -362,14 +368,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 3) void attn_t16_kernel(T16A
   for (int cb = 0; cb < D / 16; ++cb) st.o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // float32 segments shared by the workgroup's tiles first (every wave takes part:
-  // a.share guarantees that the workgroup holds NW tiles of one (batch, head))
+  // a.share guarantees that the workgroup holds NWT tiles of one (batch, head))
   if constexpr (F32) {
     if (a.share) {
       for (int si = 0; si < a.n_seg; ++si) {
         const T16Seg& sg = a.seg[si];
-        if (sg.bf16 || sg.shift < 2 || sg.count == 0 || sg.len == 0) continue;
+        if (sg.bf16 || sg.shift < SHARE_SHIFT || sg.count == 0 || sg.len == 0) continue;
         const int32_t* lst = sg.idx + ((b * a.heads_q + h) * sg.rows + (t >> sg.shift)) * sg.stride;
-        t16_shared_segment<D>(a.scale_log2, sg, lst, (b * a.heads_kv + hk) * sg.len, qb, smem, st);
+        t16_shared_segment<D, NWT>(a.scale_log2, sg, lst, (b * a.heads_kv + hk) * sg.len, qb, smem, st);
       }
     }
   }
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 3) void attn_t16_kernel(T16A
   for (int si = 0; si < a.n_seg; ++si) {
     const T16Seg& sg = a.seg[si];
     if (sg.count == 0 || sg.len == 0) continue;
-    if (F32 && a.share && !sg.bf16 && sg.shift >= 2) continue;  // done above
+    if (F32 && a.share && !sg.bf16 && sg.shift >= SHARE_SHIFT) continue;  // done above
     const int32_t* lst = sg.idx + ((b * a.heads_q + h) * sg.rows + (t >> sg.shift)) * sg.stride;
     const int64_t head_row = (b * a.heads_kv + hk) * sg.len;
     if (!F32 || sg.bf16)
@@ -409,12 +415,20 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 3) void attn_t16_kernel(T16A
 }
 
 template <bool OB, bool F32>
-hipError_t launch_t16(const T16Args& a, int d, hipStream_t s) {
+hipError_t launch_t16(T16Args a, int d, hipStream_t s) {
+  if constexpr (F32) {
+    if (d == 64 && a.lists % 16 == 0) {  // 16 tiles per workgroup share the coarse lists
+      a.share = 1;
+      dim3 grid((unsigned)(a.tiles / 16));
+      attn_t16_kernel<OB, 64, true, 16><<<grid, 16 * 64, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((unsigned)((a.tiles + NW - 1) / NW));
   if (d == 64)
-    attn_t16_kernel<OB, 64, F32><<<grid, NW * 64, 0, s>>>(a);
+    attn_t16_kernel<OB, 64, F32, NW><<<grid, NW * 64, 0, s>>>(a);
   else
-    attn_t16_kernel<OB, 128, F32><<<grid, NW * 64, 0, s>>>(a);
+    attn_t16_kernel<OB, 128, F32, NW><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -573,6 +573,31 @@ def test_attn_segments_bias_and_f32_tables(basa, tile_q):
     assert el <= lse_tol, el
 
 
+def test_attn_16_row_tiles_workgroup_size_changes_no_bit(basa):
+    # 64 lists per head run 16 tiles per workgroup (the float32 lists of shift >= 4 staged
+    # once per 16 tiles); the same first 60 tiles as a problem of their own run 4 per
+    # workgroup.  Each tile walks the same blocks in the same order either way.
+    note("attn 16-row tiles: 16 against 4 tiles per workgroup, d64")
+    g = np.random.Generator(np.random.PCG64(29))
+    d, tiles, nk = 64, 64, 1024
+    q = wl.f32_to_bf16(g.standard_normal((1, 2, tiles * 16, d)).astype(np.float32))
+    kb = wl.f32_to_bf16(g.standard_normal((1, 2, nk, d)).astype(np.float32))
+    vb = wl.f32_to_bf16(g.standard_normal((1, 2, nk, d)).astype(np.float32))
+    kf = g.standard_normal((1, 2, 256, d)).astype(np.float32)
+    vf = g.standard_normal((1, 2, 256, d)).astype(np.float32)
+    i0 = np.sort(g.integers(0, nk // 16, (1, 2, tiles, 8)), axis=-1).astype(np.int32)
+    i0[0, 1, 7, 2] = -1
+    i1 = np.sort(g.integers(0, 16, (1, 2, tiles >> 4, 8)), axis=-1).astype(np.int32)
+    i2 = np.zeros((1, 2, 1, 1), dtype=np.int32)
+    segs = lambda n: [(i0[:, :, :n], kb, vb, {}),
+                      (i1[:, :, :(n + 15) // 16], kf, vf, {"shift": 4, "bias": math.log(16)}),
+                      (i2, kf, vf, {"shift": 12, "bias": 2 * math.log(16)})]
+    o16, l16 = run_attn(basa, q, segs(tiles), 16, 16, 0.125, torch.bfloat16)
+    o4, l4 = run_attn(basa, q[:, :, :60 * 16], segs(60), 16, 16, 0.125, torch.bfloat16)
+    assert np.array_equal(o16[:, :, :60 * 16], o4)
+    assert np.array_equal(l16[:, :, :60 * 16], l4)
+
+
 @pytest.mark.parametrize("d,row_map", [(128, False), (128, True), (64, True)])
 def test_attn_16_row_tiles_f32_tables_row_map(basa, d, row_map):
     # 16-row tiles over 16-key blocks run the tile MFMA kernel: a bf16 segment and a
