@@ -378,7 +378,7 @@ def basa_pool_select(q: torch.Tensor, k: torch.Tensor, qbar: torch.Tensor, kbar_
                      idx: torch.Tensor, topk: int, *, block: int, scale: float = 1.0,
                      workspace: torch.Tensor | None = None) -> None:
     """Pool q (rows) and k (transposed) by `block` and select each query block's top-k key
-    blocks, as basa_pool + basa_pool + basa_select; one persistent launch when it applies."""
+    blocks, as basa_pool + basa_pool + basa_select (the library enqueues those three launches)."""
     prepare_pool_select(q, k, qbar, kbar_t, idx, topk, block=block, scale=scale,
                         workspace=workspace)()
 

@@ -174,9 +174,7 @@ int basa_pool_select(const basa_select_desc* d, const void* q, const void* k, in
     if (!q || !k || !qbar || !kbar_t || !idx) return BASA_E_NULLPTR;
     if (!aligned16(q) || !aligned16(k) || !aligned16(qbar) || !aligned16(kbar_t)) return BASA_E_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (basa::pool_select_fused(d, dtype, block))
-      return from_hip(basa::launch_pool_select(d, q, k, block, qbar, kbar_t, idx, s));
-    // the same three steps as separate launches
+    // the three steps as separate launches on the stream
     hipError_t e = basa::launch_pool(q, dtype, d->batch * d->heads_q, d->q_len * block, d->head_dim,
                                      block, qbar, nullptr, nullptr, BASA_F32, s);
     if (e != hipSuccess) return BASA_E_LAUNCH;

@@ -82,10 +82,6 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
                                 int32_t* idx, hipStream_t s);
 int64_t select_workspace_bytes(const basa_select_desc* d);
 int64_t pool_select_workspace_bytes(const basa_select_desc* d);
-bool pool_select_fused(const basa_select_desc* d, int dtype, int64_t block);
-hipError_t launch_pool_select(const basa_select_desc* d, const void* q, const void* k,
-                              int64_t block, double* qbar, double* kbt, int32_t* idx,
-                              hipStream_t s);
 hipError_t launch_select_change(const basa_select_desc* d, const void* q, const void* k,
                                 int dtype, int32_t* idx, hipStream_t s);
 bool attn_mfma_supported(const basa_attn_desc* d, int q_dtype, int o_dtype);

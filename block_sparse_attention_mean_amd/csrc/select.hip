@@ -542,8 +542,7 @@ __global__ __launch_bounds__(256) void select_ranges_kernel(const double* scores
 
 // ---------------------------------------------------------------------------
 // Key means staged in LDS.  The two-pass kernel below streams chunks of
-// SEL_CH channels x PART keys; the single-launch pool-and-select kernel
-// chunks of LDS_CH channels x 512 keys, SEL_RW rows per wave.
+// SEL_CH channels x PART keys.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int SEL_CH = 8;  // channels per staged chunk
@@ -551,10 +550,6 @@ constexpr int SEL_CH = 8;  // channels per staged chunk
 constexpr int SEL_BYTES = SEL_CH * 8 * 64 * 8;  // 8 channels x 512 keys of float64
 __shared__ __attribute__((aligned(16))) uint8_t s_sel0[SEL_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t s_sel1[SEL_BYTES];
-
-constexpr int LDS_CH = 4;                        // channels per staged chunk (single launch)
-constexpr int LDS_BYTES = LDS_CH * 8 * 64 * 8;   // 4 channels x 512 keys of float64
-constexpr int SEL_RW = 4;                        // rows per wave (single launch)
 
 // ---------------------------------------------------------------------------
 // 512 candidates (no parent list) on the float64 matrix core
@@ -989,247 +984,6 @@ __global__ __launch_bounds__(256) void select_change_kernel(const T* __restrict_
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pooling and selection in one persistent launch (basa_pool_select): the key
-// means of a key head are pooled by key tasks; a selection task pools its own
-// 16 query blocks into LDS, waits until its key head's means are complete,
-// then scores its rows with vector FMAs over 4-channel LDS chunks and selects
-// with wave_topk.  Tasks are
-// taken from one ticket counter in this order, per batch: stage s holds the
-// key tasks of key head s/group (at its first query head) and the selection
-// tasks of query head s - PS_LAG, so a selection task is taken after every
-// key task it waits for: the tasks it depends on are already running on
-// workgroups that never wait, and every wait ends.  A key task publishes its
-// means with an agent-scope release (the L2s of the XCDs are not coherent)
-// and a per-key-head count; a selection task reads the count, then acquires.
-// The query reads of the selection tasks and the key reads of the key tasks
-// stream from HBM while other workgroups on the same CUs score, which hides
-// most of the selection behind the pooling's memory time.
-// ---------------------------------------------------------------------------
-constexpr int PS_ROWS = 16;        // query blocks per selection task (4 rows per wave)
-constexpr int PS_KBLK = 16;        // key blocks per key task
-constexpr int PS_LAG = 2;          // stages between a key head's pooling and its selection
-constexpr int PS_SPIN = 1 << 22;   // bound of a selection task's wait (about a second)
-constexpr int PS_DMAX = 128;       // largest head_dim (query means of a task in LDS)
-constexpr int PS_RED = 32768;      // bytes of the reduction / key-stage buffer
-
-struct PoolSelArgs {
-  const uint16_t* xq;   // [B][Hq][len_q][d] bf16
-  const uint16_t* xk;   // [B][Hkv][len_k][d] bf16
-  double* qbar;         // [B][Hq][nb_q][d] or null
-  double* kbt;          // [B][Hkv][d][nb_k]
-  int32_t* idx;         // [B][Hq][nb_q][topk]
-  int32_t* ctr;         // [0] ticket, [1] wait-bound flag, [2 + b*Hkv + hk] key tasks done
-  int64_t len_q, len_k;
-  int d, block, nb_q, nb_k, topk, heads_q, heads_kv, group, batch, tk, ts;
-  int64_t tasks;
-};
-
-__device__ __forceinline__ void ps_bf16x8_add(u32x4_sel r, double* acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] += (double)bf16_bits_to_f32(r[i] & 0xFFFFu);
-    acc[2 * i + 1] += (double)bf16_bits_to_f32(r[i] >> 16);
-  }
-}
-
-// Means of two consecutive blocks (block rows each) of one head's bf16 rows,
-// starting at block g0, combined through `red` (fp64 [2][256/(d/8)][d]) in a
-// fixed order; out(s2, c, mean) receives each result.  Every thread calls it.
-template <typename Out>
-__device__ __forceinline__ void ps_pool_pair(const uint16_t* x, int d, int block, int g0,
-                                             double* red, Out out) {
-  const int cols8 = d >> 3, groups = 256 / cols8;
-  const int t = threadIdx.x, rg = t / cols8, c8 = t - rg * cols8;
-  double acc[2][8];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[s2][i] = 0.0;
-  if (rg < groups) {
-    const uint16_t* src = x + (int64_t)g0 * block * d + c8 * 8;
-    int r = rg;
-    for (; r + 7 * groups < block; r += 8 * groups) {
-      u32x4_sel raw[2][8];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          raw[s2][u] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_sel*>(src + ((int64_t)s2 * block + r + u * groups) * d));
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ps_bf16x8_add(raw[s2][u], acc[s2]);
-    }
-    for (; r < block; r += groups) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        ps_bf16x8_add(__builtin_nontemporal_load(
-                          reinterpret_cast<const u32x4_sel*>(src + ((int64_t)s2 * block + r) * d)),
-                      acc[s2]);
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) red[(s2 * groups + rg) * d + c8 * 8 + i] = acc[s2][i];
-  }
-  __syncthreads();
-  const int used = groups < block ? groups : block;
-  for (int e = t; e < 2 * d; e += 256) {
-    const int s2 = e / d, c = e - s2 * d;
-    double sum = 0.0;
-    for (int r = 0; r < used; ++r) sum += red[(s2 * groups + r) * d + c];
-    out(s2, c, sum / (double)block);
-  }
-  __syncthreads();  // `red` is reused by the next call
-}
-
-__global__ __launch_bounds__(256, 3) void pool_select_kernel(PoolSelArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_red[PS_RED];
-  __shared__ double s_qm[PS_ROWS * PS_DMAX];
-  __shared__ int64_t s_task;
-  double* red = reinterpret_cast<double*>(s_red);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int d = a.d;
-  const int64_t per_batch = (int64_t)a.heads_kv * a.tk + (int64_t)a.heads_q * a.ts;
-
-  for (;;) {
-    if (threadIdx.x == 0) s_task = atomicAdd(&a.ctr[0], 1);
-    __syncthreads();
-    const int64_t task = s_task;
-    __syncthreads();
-    if (task >= a.tasks) break;
-    const int b = (int)(task / per_batch);
-    int64_t r = task - (int64_t)b * per_batch;
-    int kind = -1, head = 0, j = 0;   // kind 0: key task, 1: selection task
-    for (int st = 0; st < a.heads_q + PS_LAG; ++st) {
-      const int ck = (st < a.heads_q && st % a.group == 0) ? a.tk : 0;
-      const int cs = (st >= PS_LAG && st - PS_LAG < a.heads_q) ? a.ts : 0;
-      if (r < ck) { kind = 0; head = st / a.group; j = (int)r; break; }
-      r -= ck;
-      if (r < cs) { kind = 1; head = st - PS_LAG; j = (int)r; break; }
-      r -= cs;
-    }
-    if (kind < 0) continue;  // not reached: every ticket below a.tasks names a task
-
-    if (kind == 0) {
-      // key task: means of key blocks [PS_KBLK j, PS_KBLK j + PS_KBLK) of key head `head`
-      const uint16_t* x = a.xk + ((int64_t)b * a.heads_kv + head) * a.len_k * d;
-      double* kt = a.kbt + ((int64_t)b * a.heads_kv + head) * d * a.nb_k;
-      for (int g0 = j * PS_KBLK; g0 < j * PS_KBLK + PS_KBLK; g0 += 2)
-        ps_pool_pair(x, d, a.block, g0, red, [&](int s2, int c, double m) {
-          kt[(int64_t)c * a.nb_k + g0 + s2] = m;
-        });
-      __threadfence();   // this thread's means are visible device-wide
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(&a.ctr[2 + b * a.heads_kv + head], 1, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      continue;
-    }
-
-    // selection task: query blocks [PS_ROWS j, PS_ROWS j + PS_ROWS) of query head `head`
-    const int h = head, hk = h / a.group;
-    const int row_base = j * PS_ROWS;
-    {
-      const uint16_t* x = a.xq + ((int64_t)b * a.heads_q + h) * a.len_q * d;
-      for (int p = 0; p < PS_ROWS; p += 2)
-        ps_pool_pair(x, d, a.block, row_base + p, red, [&](int s2, int c, double m) {
-          s_qm[(p + s2) * d + c] = m;
-          if (a.qbar) a.qbar[(((int64_t)b * a.heads_q + h) * a.nb_q + row_base + p + s2) * d + c] = m;
-        });
-    }
-    // wait until every key task of the key head is done, then acquire its means
-    if (threadIdx.x == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(&a.ctr[2 + b * a.heads_kv + hk], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) < a.tk) {
-        if (++spins > PS_SPIN) {
-          __hip_atomic_fetch_or(&a.ctr[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    constexpr int KPL = 8;  // 512 keys
-    const double* kt = a.kbt + ((int64_t)b * a.heads_kv + hk) * d * a.nb_k;
-    double acc[SEL_RW][KPL];
-#pragma unroll
-    for (int i = 0; i < SEL_RW; ++i)
-#pragma unroll
-      for (int q2 = 0; q2 < KPL; ++q2) acc[i][q2] = 0.0;
-    uint8_t* buf0 = s_red;
-    uint8_t* buf1 = s_red + LDS_BYTES;
-    auto dma = [&](uint8_t* dst, const double* src) {
-#pragma unroll
-      for (int i = 0; i < LDS_BYTES / 4096; ++i)
-        __builtin_amdgcn_global_load_lds(src + (i * 4096 + threadIdx.x * 16) / 8,
-                                         (lds_void*)(dst + i * 4096 + wave * 1024), 16, 0, 0);
-    };
-    auto chunk = [&](const uint8_t* buf, int c0) {
-      const double* kc = reinterpret_cast<const double*>(buf);
-#pragma unroll 2
-      for (int cc = 0; cc < LDS_CH; ++cc) {
-        double kv[KPL];
-#pragma unroll
-        for (int q2 = 0; q2 < KPL; ++q2) kv[q2] = kc[cc * KPL * 64 + lane + 64 * q2];
-#pragma unroll
-        for (int i = 0; i < SEL_RW; ++i) {
-          const double qv = s_qm[(wave * SEL_RW + i) * d + c0 + cc];
-#pragma unroll
-          for (int q2 = 0; q2 < KPL; ++q2) acc[i][q2] = __builtin_fma(qv, kv[q2], acc[i][q2]);
-        }
-      }
-    };
-    const int n_chunk = d / LDS_CH;
-    const int64_t chunk_elems = (int64_t)LDS_CH * a.nb_k;
-    dma(buf0, kt);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    for (int k = 0; k < n_chunk; k += 2) {
-      dma(buf1, kt + (k + 1) * chunk_elems);
-      chunk(buf0, k * LDS_CH);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (k + 2 < n_chunk) dma(buf0, kt + (k + 2) * chunk_elems);
-      chunk(buf1, (k + 1) * LDS_CH);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int i = 0; i < SEL_RW; ++i) {
-      const int row = row_base + wave * SEL_RW + i;
-      uint64_t key[KPL];
-      bool valid[KPL], sel[KPL];
-#pragma unroll
-      for (int q2 = 0; q2 < KPL; ++q2) {
-        valid[q2] = true;
-        key[q2] = ordered_key(acc[i][q2]);
-      }
-      wave_topk<KPL>(key, valid, a.topk, below, sel);
-      int32_t* out = a.idx + (((int64_t)b * a.heads_q + h) * a.nb_q + row) * a.topk;
-      int base = 0;
-#pragma unroll
-      for (int q2 = 0; q2 < KPL; ++q2) {
-        const uint64_t m = __ballot(sel[q2]);
-        if (sel[q2]) out[base + popc64(m & below)] = lane + 64 * q2;
-        base += popc64(m);
-      }
-    }
-    __syncthreads();  // the stage buffers and the query means are reused by the next task
-  }
-}
-
-__global__ void ps_clear_kernel(int32_t* ctr, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ctr[i] = 0;
-}
-
 }  // namespace
 
 int64_t select_workspace_bytes(const basa_select_desc* d) {
@@ -1318,58 +1072,7 @@ hipError_t launch_select_blocks(const basa_select_desc* d, const double* q, cons
   return launch_kr<64, 1>(a, d->batch, s);
 }
 
-int64_t pool_select_workspace_bytes(const basa_select_desc* d) {
-  return ((2 + d->batch * d->heads_kv) * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
-}
-
-// The single-launch form is switched off: its first GPU run (64K workload)
-// produced no result within 180 s and was stopped.  The cause is not known
-// (the decoding and dependency order of the tasks were checked on the CPU;
-// visibility of the per-key-head counts across XCDs, or the polling of about
-// 700 waiting workgroups on 32 counts, are suspected, not shown), so
-// basa_pool_select runs the three separate launches until one is found.
-bool pool_select_fused(const basa_select_desc* d, int dtype, int64_t block) {
-  constexpr bool kSingleLaunch = false;
-  return kSingleLaunch && dtype == BASA_BF16 && d->keys == 512 && d->head_dim <= PS_DMAX &&
-         d->head_dim % (2 * LDS_CH) == 0 && d->q_len % PS_ROWS == 0 && d->keys % PS_KBLK == 0 &&
-         d->topk >= 1 && d->topk <= 512 && block >= 1 && d->batch >= 1 && d->q_len >= 1 &&
-         d->workspace && d->workspace_bytes >= pool_select_workspace_bytes(d) &&
-         (reinterpret_cast<uintptr_t>(d->workspace) & 3) == 0;
-}
-
-hipError_t launch_pool_select(const basa_select_desc* d, const void* q, const void* k,
-                              int64_t block, double* qbar, double* kbt, int32_t* idx,
-                              hipStream_t s) {
-  PoolSelArgs a;
-  a.xq = static_cast<const uint16_t*>(q);
-  a.xk = static_cast<const uint16_t*>(k);
-  a.qbar = qbar;
-  a.kbt = kbt;
-  a.idx = idx;
-  a.ctr = static_cast<int32_t*>(d->workspace);
-  a.d = (int)d->head_dim;
-  a.block = (int)block;
-  a.nb_q = (int)d->q_len;
-  a.nb_k = (int)d->keys;
-  a.len_q = d->q_len * block;
-  a.len_k = d->keys * block;
-  a.topk = d->topk;
-  a.heads_q = (int)d->heads_q;
-  a.heads_kv = (int)d->heads_kv;
-  a.group = (int)(d->heads_q / d->heads_kv);
-  a.batch = (int)d->batch;
-  a.tk = a.nb_k / PS_KBLK;
-  a.ts = a.nb_q / PS_ROWS;
-  a.tasks = d->batch * ((int64_t)a.heads_kv * a.tk + (int64_t)a.heads_q * a.ts);
-  const int n_ctr = (int)(2 + d->batch * d->heads_kv);
-  ps_clear_kernel<<<1, 256, 0, s>>>(a.ctr, n_ctr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // three workgroups per CU on 256 CUs; later workgroups find the queue empty
-  const int64_t wgs = a.tasks < 768 ? a.tasks : 768;
-  pool_select_kernel<<<dim3((unsigned)wgs), 256, 0, s>>>(a);
-  return hipGetLastError();
-}
+int64_t pool_select_workspace_bytes(const basa_select_desc*) { return 0; }
 
 hipError_t launch_select_change(const basa_select_desc* d, const void* q, const void* k, int dtype,
                                 int32_t* idx, hipStream_t s) {

@@ -32,7 +32,7 @@ from . import (MOMENTS_KEY, MOMENTS_QUERY, PERMUTE_GATHER, PERMUTE_SCATTER, SELE
                basa_permute, basa_pool, basa_pool_moments, basa_pool_pyramid, basa_rank,
                basa_rank_workspace,
                basa_select, basa_select_ranges, basa_select_workspace, kv_segment, prepare_attn,
-               prepare_merge, prepare_pool, prepare_select)
+               prepare_merge, prepare_pool, prepare_pool_select, prepare_select)
 
 
 def _empty(*shape, dtype, like):
@@ -72,10 +72,10 @@ class BaForward:
         self.lse = _empty(b, h, length, dtype=torch.float32, like=q)
         self._select = None
         if beta is None:
-            # the selection stage's three calls, validated once
-            self._select = [prepare_pool(q, block, mean_rows=self.qbar),
-                            prepare_pool(k, block, mean_cols=self.kbt),
-                            prepare_select(self.qbar, self.kbt, self.idx, topk, scale=self.scale)]
+            # the selection stage (pool Q and K, score, top-k) as one call, validated once:
+            # the library overlaps the query pooling with the selection where it can
+            self._select = [prepare_pool_select(q, k, self.qbar, self.kbt, self.idx, topk, block=block,
+                                                scale=self.scale)]
         # the attention call, validated once, with the workspace in which the
         # library orders the query tiles (the same output without it)
         seg = kv_segment(self.idx, k, v)

@@ -251,19 +251,17 @@ int basa_select(const basa_select_desc* desc, const void* q, const void* k, int 
  *   qbar    device float64 [batch][heads_q][q_len][head_dim] (written)
  *   kbar_t  device float64 [batch][heads_kv][head_dim][keys] (written)
  *   idx     device int32 [batch][heads_q][q_len][topk] (written)
- * It runs as the three separate launches.  A single persistent launch (key
- * tasks pooling the key heads, selection tasks pooling their own query blocks
- * and waiting on per-key-head counts in desc->workspace) is written but
- * switched off: its first run did not finish in 180 s, for a reason not yet
- * shown.  desc->workspace is accepted and unused.
+ * It enqueues the three launches (query means, key means, selection) on the
+ * stream.  desc->workspace is accepted and unused.
  * Errors: as basa_pool and basa_select, plus BASA_E_UNSUPPORTED for another
  * mode, a row map or a parent list, and BASA_E_NULLPTR for a NULL output.
  */
 int basa_pool_select(const basa_select_desc* desc, const void* q, const void* k, int dtype,
                      int64_t block, double* qbar, double* kbar_t, int32_t* idx, void* stream);
 
-/* basa_pool_select_workspace - bytes of workspace basa_pool_select uses for
- * its single-launch form (a few counters).  Errors: BASA_E_NULLPTR. */
+/* basa_pool_select_workspace - bytes of workspace basa_pool_select uses: 0
+ * (kept so that callers written against a workspace-taking form still work).
+ * Errors: BASA_E_NULLPTR. */
 int basa_pool_select_workspace(const basa_select_desc* desc, int64_t* bytes);
 
 /*
