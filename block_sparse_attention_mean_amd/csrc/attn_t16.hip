@@ -7,7 +7,7 @@
 // segments with an additive logit bias per level.  Online softmax per 16-key
 // block.
 //
-// One wave computes one tile; a workgroup holds four waves (sixteen for the
+// One wave computes one tile; a workgroup holds four waves (eight for the
 // log-linear levels).  Float32 segments whose list row is shared by the
 // workgroup's tiles are staged once per
 // workgroup (barrier-synchronised); everything else each wave walks alone.  Per 16-key block the wave forms S^T = K Q^T with
@@ -30,7 +30,7 @@
 namespace basa {
 namespace {
 
-constexpr int NW = 4;          // waves (tiles) per workgroup (16 for the log-linear coarse levels)
+constexpr int NW = 4;          // waves (tiles) per workgroup (8 for the log-linear coarse levels)
 constexpr float kLazy = 8.0f;  // log2 headroom before the max is raised
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -318,14 +318,17 @@ __device__ __forceinline__ void t16_shared_segment(float scale_log2, const T16Se
 }
 
 // F32: some segment has a float32 table (without it the float32 path, and its
-// registers, are not compiled in).  NWT tiles (waves) per workgroup: 4, or 16
-// when the float32 lists repeat over 16 consecutive tiles (the log-linear
+// registers, are not compiled in).  NWT tiles (waves) per workgroup: 4, or 8
+// when the float32 lists repeat over 8 consecutive tiles (the log-linear
 // levels above the first: a level-2 block's 16 tiles share their level-1
-// candidates), so that each coarse block is read and split once per 16 tiles.
+// candidates), so that each coarse block is read and split once per 8 tiles;
+// two such workgroups share a CU (74 KB of LDS each), so one waits on its
+// loads while the other computes.  (The second launch bound is the minimum
+// number of waves per SIMD: 4, i.e. at most 128 registers.)
 template <bool O_BF16, int D, bool F32, int NWT>
-__global__ __launch_bounds__(NWT * 64, NWT == 16 ? 1 : (D == 64 ? 4 : 3)) void attn_t16_kernel(T16Args a) {
+__global__ __launch_bounds__(NWT * 64, (D == 64 || NWT == 8) ? 4 : 3) void attn_t16_kernel(T16Args a) {
   constexpr int CPL = D / 4;
-  constexpr int SHARE_SHIFT = NWT == 16 ? 4 : 2;  // list rows with this shift repeat over the workgroup
+  constexpr int SHARE_SHIFT = NWT == 8 ? 3 : 2;  // list rows with this shift repeat over the workgroup
   // per-wave areas; with float32 segments also the shared area, which they alias
   // (the shared segments are done, behind a barrier, before any per-wave area is used)
   constexpr int SMEM = (F32 && T16Shared<D, NWT>::BYTES > NWT * T16Lds<D>::BYTES)
@@ -417,10 +420,10 @@ __global__ __launch_bounds__(NWT * 64, NWT == 16 ? 1 : (D == 64 ? 4 : 3)) void a
 template <bool OB, bool F32>
 hipError_t launch_t16(T16Args a, int d, hipStream_t s) {
   if constexpr (F32) {
-    if (d == 64 && a.lists % 16 == 0) {  // 16 tiles per workgroup share the coarse lists
+    if (d == 64 && a.lists % 8 == 0) {  // 8 tiles per workgroup share the coarse lists
       a.share = 1;
-      dim3 grid((unsigned)(a.tiles / 16));
-      attn_t16_kernel<OB, 64, true, 16><<<grid, 16 * 64, 0, s>>>(a);
+      dim3 grid((unsigned)(a.tiles / 8));
+      attn_t16_kernel<OB, 64, true, 8><<<grid, 8 * 64, 0, s>>>(a);
       return hipGetLastError();
     }
   }

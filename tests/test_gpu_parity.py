@@ -574,10 +574,10 @@ def test_attn_segments_bias_and_f32_tables(basa, tile_q):
 
 
 def test_attn_16_row_tiles_workgroup_size_changes_no_bit(basa):
-    # 64 lists per head run 16 tiles per workgroup (the float32 lists of shift >= 4 staged
-    # once per 16 tiles); the same first 60 tiles as a problem of their own run 4 per
+    # 64 lists per head run 8 tiles per workgroup (the float32 lists of shift >= 3 staged
+    # once per 8 tiles); the same first 60 tiles as a problem of their own run 4 per
     # workgroup.  Each tile walks the same blocks in the same order either way.
-    note("attn 16-row tiles: 16 against 4 tiles per workgroup, d64")
+    note("attn 16-row tiles: 8 against 4 tiles per workgroup, d64")
     g = np.random.Generator(np.random.PCG64(29))
     d, tiles, nk = 64, 64, 1024
     q = wl.f32_to_bf16(g.standard_normal((1, 2, tiles * 16, d)).astype(np.float32))
