@@ -224,16 +224,15 @@ def prepare_pool_pyramid(xs, block: int, outputs):
     outer = 1
     for s in lead:
         outer *= s
-    arr = (PyramidTensor * n)()
+    # every shape first, then the device pointers
     copy_dts = set()
     for i, x in enumerate(xs):
         if x.shape != xs[0].shape or x.dtype != xs[0].dtype:
             raise ValueError("pyramid inputs must share shape and dtype")
         if len(outputs[i]) != levels:
             raise ValueError("every tensor needs the same number of levels")
-        arr[i].x = _ptr(x)
         span = 1
-        for lv, (rows, cols, copy) in enumerate(outputs[i]):
+        for rows, cols, copy in outputs[i]:
             span *= block
             if block > 0 and length % span == 0:   # otherwise the C call reports BASA_E_SHAPE
                 nb = length // span
@@ -242,10 +241,14 @@ def prepare_pool_pyramid(xs, block: int, outputs):
                 _shape("mean_copy", copy, (*lead, nb, d))
             if copy is not None:
                 copy_dts.add(_dt(copy))
-            arr[i].level[lv] = PyramidLevel(_ptr(rows), _ptr(cols), _ptr(copy))
     if len(copy_dts) > 1:
         raise ValueError("every mean_copy of one pyramid call must have the same dtype")
     copy_dt = copy_dts.pop() if copy_dts else F32
+    arr = (PyramidTensor * n)()
+    for i, x in enumerate(xs):
+        arr[i].x = _ptr(x)
+        for lv, (rows, cols, copy) in enumerate(outputs[i]):
+            arr[i].level[lv] = PyramidLevel(_ptr(rows), _ptr(cols), _ptr(copy))
     args = (arr, n, _dt(xs[0]), outer, length, d, block, levels, copy_dt)
     return _prepared("basa_pool_pyramid", lib.basa_pool_pyramid, args, (xs, outputs, arr))
 

@@ -42,6 +42,23 @@ def test_pool_outputs():
     shape_error(basa.basa_pool, x, 64, mean_copy=z(1, 2, 4, 32))
 
 
+def test_pool_pyramid_outputs():
+    xs = [z(1, 2, 4096, 64, dtype=bf16) for _ in range(3)]
+
+    def outs(l1_rows=(1, 2, 256, 64), l2_cols=(1, 2, 64, 16)):
+        return [[(z(*l1_rows, dtype=f64), None, z(1, 2, 256, 64)),
+                 (z(1, 2, 16, 64, dtype=f64), z(*l2_cols, dtype=f64), None)] for _ in range(3)]
+    reaches_device_check(basa.basa_pool_pyramid, xs, 16, outs())
+    shape_error(basa.basa_pool_pyramid, xs, 16, outs(l1_rows=(1, 2, 255, 64)))   # level-1 rows
+    shape_error(basa.basa_pool_pyramid, xs, 16, outs(l2_cols=(1, 2, 16, 64)))    # level-2 layout
+    shape_error(basa.basa_pool_pyramid, [xs[0], z(1, 2, 2048, 64, dtype=bf16)], 16, outs()[:2])
+    shape_error(basa.basa_pool_pyramid, xs, 16, [outs()[0], outs()[1][:1], outs()[2]])  # levels
+    mixed = outs()
+    mixed[1][0] = (mixed[1][0][0], None, z(1, 2, 256, 64, dtype=bf16))             # copy dtypes
+    shape_error(basa.basa_pool_pyramid, xs, 16, mixed)
+    shape_error(basa.basa_pool_pyramid, xs * 2, 16, outs() * 2)                    # six tensors
+
+
 # ---------------------------------------------------------------- select
 
 def sel_args(hq=4, hkv=2, nq=8, nk=16, d=64, topk=4):
