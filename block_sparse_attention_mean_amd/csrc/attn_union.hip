@@ -139,7 +139,7 @@ __global__ __launch_bounds__(UW * 64) void union_walk_kernel(UnionArgs a) {
   // how often each row lists each block of this chunk.  Every list entry and
   // query value a thread needs is requested before the first one is used.
   for (int e = threadIdx.x; e < UCB * UMAX_R; e += UW * 64) s_cnt[e / UMAX_R][e % UMAX_R] = 0;
-  if (threadIdx.x < R) s_tok[threadIdx.x] = row_token(a, b, threadIdx.x);
+  if ((int)threadIdx.x < R) s_tok[threadIdx.x] = row_token(a, b, threadIdx.x);
   __syncthreads();
   constexpr int NT = UW * 64;
   for (int e0 = 0; e0 < R * a.count; e0 += 8 * NT) {

@@ -47,12 +47,6 @@ __device__ __forceinline__ double uniform_ld(const double* p) {
   return *(const_f64*)p;
 }
 
-__device__ __forceinline__ uint64_t readfirstlane64(uint64_t x) {
-  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-  const uint32_t h = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
-  return ((uint64_t)h << 32) | l;
-}
-
 // Largest / smallest 32-bit value over the wave (every lane active): DPP
 // exchanges inside each row of 16 lanes (pairs, quad halves, half-row mirror,
 // row mirror), then the four rows' results read into scalars.
