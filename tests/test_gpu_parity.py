@@ -98,6 +98,9 @@ def _pyramid_inputs(case):
     if case == "bf16_copies":    # bf16 copies, two levels, block 8, head_dim 128
         x = wl.make_dlm(32, heads=2, tokens=8 * 8 * 6, head_dim=128)
         return [x["k"], x["v"]], 8, 2, torch.bfloat16
+    if case == "bf16_wide":       # block 32 x head_dim 128: 512 items for 256 threads per workgroup
+        x = wl.make_dlm(34, heads=2, tokens=32 * 32 * 3, head_dim=128)
+        return [x["q"], x["k"]], 32, 2, torch.float32
     if case == "bf16_one_level":  # one level: the plain pooling call per tensor
         x = wl.make_dlm(33, heads=2, tokens=512, head_dim=64)
         return [x["q"], x["k"], x["v"]], 32, 1, torch.float32
@@ -108,8 +111,8 @@ def _pyramid_inputs(case):
         torch.float32
 
 
-@pytest.mark.parametrize("case", ["bf16_llsa", "bf16_copies", "bf16_one_level", "f32_ragged",
-                                  "f64_four_levels"])
+@pytest.mark.parametrize("case", ["bf16_llsa", "bf16_copies", "bf16_wide", "bf16_one_level",
+                                  "f32_ragged", "f64_four_levels"])
 def test_pool_pyramid_equals_chained_pooling(basa, case):
     """basa_pool_pyramid against basa_pool applied level by level (level l from the float64
     rows of level l - 1): every output identical bit for bit.  For bf16 inputs every level also
